@@ -1,0 +1,265 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The parity tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library; the HIP library never
+ * does, and the two share no code, header, table or helper.
+ *
+ * What it computes is the plain definition, not the streaming method that the
+ * GPU kernels use:
+ *
+ *   * three-pass safe softmax: pass 1 takes the maximum, pass 2 sums
+ *     exp(x - max), pass 3 divides ('Online Softmax -- the mathematical heart
+ *     of FlashAttention' section 1; 'Online softmax in attention -- why and
+ *     how', section "The textbook softmax: stable, but two passes");
+ *   * attention as softmax over one query's scores applied to the value rows,
+ *     A_i = sum_j softmax(s_i)_j V_j with s_ij = scale * q_i . k_j
+ *     ('Online Softmax -- the mathematical heart of FlashAttention' section 5;
+ *     'Online Softmax & FlashAttention' (interview lesson), Step 2, where the
+ *     scores are q K^T times scale with scale = 1/sqrt(d) by default);
+ *   * the row log-sum-exp LSE = m + ln l, which is -inf for a row with no
+ *     visible key ('Online Softmax & FlashAttention', Step 1 and Step 3).
+ *
+ * Readings where the pages leave a step open (each listed in the design notes):
+ *   * a masked key is left out of the softmax; a row with no visible key has
+ *     m = -inf, l = 0, output 0 and LSE = -inf ('Online Softmax & FlashAttention',
+ *     Step 1: the fully masked row of the chunking example);
+ *   * causal visibility is key j <= query i + (Nk - N): the queries are the last
+ *     N positions of the key sequence, which is j <= i for N = Nk
+ *     ('Online softmax in attention -- why and how', section "Why this matters
+ *     for attention specifically");
+ *   * key_lens[b] (clamped to [0, Nk]) hides keys j >= key_lens[b] of batch b
+ *     from every query; it combines with the causal rule by AND;
+ *   * inputs are the stored fp32 / bf16 values widened exactly to fp64.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread oracle.c -lm
+ * (no fast-math: -inf must stay IEEE -inf).
+ *
+ * Parity pins (tests/test_oracle.py): the worked softmax examples printed on
+ * the pages, the chunk-merge invariant of 'Online Softmax & FlashAttention'
+ * Step 1, the tiled V1 shapes of its Step 2, closed forms, invariants and a
+ * library cross-check.  Every exported function here is pinned.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
+
+/* Exact widening of one stored element to fp64. */
+static double widen(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORACLE_F64)
+        return ((const double *)base)[idx];
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    {
+        uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+}
+
+/*
+ * Three-pass safe softmax of x[0..n).  Entries equal to -inf are masked and
+ * get weight 0.  If every entry is masked (or n == 0): m = -inf, l = 0 and
+ * y = 0.  Outputs: y[0..n) (may be NULL), *m_out = max, *l_out = sum of
+ * exp(x - max).  Returns 0.
+ */
+int oracle_softmax_f64(const double *x, long n, double *y, double *m_out, double *l_out)
+{
+    double m = -INFINITY, l = 0.0;
+    long j;
+    for (j = 0; j < n; ++j)                 /* pass 1: maximum */
+        if (x[j] > m)
+            m = x[j];
+    if (m == -INFINITY) {
+        if (y)
+            for (j = 0; j < n; ++j)
+                y[j] = 0.0;
+        *m_out = m;
+        *l_out = 0.0;
+        return 0;
+    }
+    for (j = 0; j < n; ++j)                 /* pass 2: normaliser */
+        l += exp(x[j] - m);
+    if (y)
+        for (j = 0; j < n; ++j)             /* pass 3: divide */
+            y[j] = exp(x[j] - m) / l;
+    *m_out = m;
+    *l_out = l;
+    return 0;
+}
+
+typedef struct {
+    const void *Q, *K, *V;
+    int dtype;
+    long B, H, N, Nk, d;
+    double scale;
+    int causal;
+    const int32_t *key_lens;    /* host int32[B] or NULL */
+    long nrows;
+    const int64_t *rows;        /* flat indices (b*H + h)*N + i, or NULL = all */
+    double *O;                  /* [nrows, d] */
+    double *LSE;                /* [nrows] */
+} attn_args;
+
+typedef struct {
+    const attn_args *a;
+    long begin, end;            /* range of output rows */
+    int status;
+} attn_job;
+
+/* Number of keys visible to query i of batch b: always a prefix [0, n). */
+static long visible_keys(const attn_args *a, long b, long i)
+{
+    long n = a->Nk;
+    if (a->key_lens) {
+        long kl = a->key_lens[b];
+        if (kl < 0)
+            kl = 0;
+        if (kl > a->Nk)
+            kl = a->Nk;
+        n = kl;
+    }
+    if (a->causal) {
+        long lim = i + (a->Nk - a->N) + 1;  /* keys j <= i + Nk - N */
+        if (lim < 0)
+            lim = 0;
+        if (lim < n)
+            n = lim;
+    }
+    return n;
+}
+
+static void attend_row(const attn_args *a, long out_row, double *s)
+{
+    long flat = a->rows ? (long)a->rows[out_row] : out_row;
+    long bh = flat / a->N, i = flat % a->N, b = bh / a->H;
+    long d = a->d, Nk = a->Nk, nvis = visible_keys(a, b, i);
+    size_t qoff = ((size_t)bh * a->N + i) * d, kvoff = (size_t)bh * Nk * d;
+    double *o = a->O + (size_t)out_row * d;
+    double m = -INFINITY, l = 0.0;
+    long j, c;
+
+    for (c = 0; c < d; ++c)
+        o[c] = 0.0;
+    if (nvis == 0) {                        /* fully masked row */
+        a->LSE[out_row] = -INFINITY;
+        return;
+    }
+    for (j = 0; j < nvis; ++j) {            /* scores s_j = scale * q . k_j */
+        double dot = 0.0;
+        for (c = 0; c < d; ++c)
+            dot += widen(a->Q, a->dtype, qoff + c) * widen(a->K, a->dtype, kvoff + (size_t)j * d + c);
+        s[j] = a->scale * dot;
+    }
+    for (j = 0; j < nvis; ++j)              /* pass 1: maximum */
+        if (s[j] > m)
+            m = s[j];
+    for (j = 0; j < nvis; ++j)              /* pass 2: normaliser */
+        l += exp(s[j] - m);
+    for (j = 0; j < nvis; ++j) {            /* pass 3: weighted values / l */
+        double p = exp(s[j] - m) / l;
+        for (c = 0; c < d; ++c)
+            o[c] += p * widen(a->V, a->dtype, kvoff + (size_t)j * d + c);
+    }
+    a->LSE[out_row] = m + log(l);
+}
+
+static void *attend_job(void *arg)
+{
+    attn_job *job = (attn_job *)arg;
+    const attn_args *a = job->a;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(a->Nk > 0 ? a->Nk : 1));
+    long r;
+    if (!s) {
+        job->status = -2;
+        return NULL;
+    }
+    for (r = job->begin; r < job->end; ++r)
+        attend_row(a, r, s);
+    free(s);
+    job->status = 0;
+    return NULL;
+}
+
+/*
+ * Attention forward in fp64 for every query row (rows == NULL, nrows must be
+ * B*H*N) or for the listed flat rows (b*H + h)*N + i.
+ * Q: [B,H,N,d], K and V: [B,H,Nk,d], row-major, element type `dtype`
+ * (0 = fp64, 1 = fp32, 2 = bf16 bits).  key_lens: host int32[B] or NULL.
+ * O: fp64 [nrows, d]; LSE: fp64 [nrows].  nthreads <= 0 means 1.
+ * Returns 0, -1 for invalid arguments, -2 when memory runs out.
+ */
+int oracle_attention_f64(const void *Q, const void *K, const void *V, int dtype,
+                         long B, long H, long N, long Nk, long d, double scale, int causal,
+                         const int32_t *key_lens, long nrows, const int64_t *rows,
+                         double *O, double *LSE, int nthreads)
+{
+    attn_args a;
+    attn_job *jobs;
+    pthread_t *tids;
+    char *started;
+    long r, per, t;
+    int status = 0;
+
+    if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0 || nrows < 0 ||
+        dtype < ORACLE_F64 || dtype > ORACLE_BF16 || (causal != 0 && causal != 1))
+        return -1;
+    if (!rows && nrows != B * H * N)
+        return -1;
+    if (rows)
+        for (r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= B * H * N)
+                return -1;
+    if (nrows == 0)
+        return 0;
+    if (!O || !LSE || !Q || (Nk > 0 && (!K || !V)))
+        return -1;
+
+    a.Q = Q; a.K = K; a.V = V; a.dtype = dtype;
+    a.B = B; a.H = H; a.N = N; a.Nk = Nk; a.d = d;
+    a.scale = scale; a.causal = causal; a.key_lens = key_lens;
+    a.nrows = nrows; a.rows = rows; a.O = O; a.LSE = LSE;
+
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    jobs = (attn_job *)calloc((size_t)nthreads, sizeof *jobs);
+    tids = (pthread_t *)calloc((size_t)nthreads, sizeof *tids);
+    started = (char *)calloc((size_t)nthreads, 1);
+    if (!jobs || !tids || !started) {
+        free(jobs);
+        free(tids);
+        free(started);
+        return -2;
+    }
+    per = (nrows + nthreads - 1) / nthreads;
+    for (t = 0; t < nthreads; ++t) {
+        jobs[t].a = &a;
+        jobs[t].begin = t * per < nrows ? t * per : nrows;
+        jobs[t].end = (t + 1) * per < nrows ? (t + 1) * per : nrows;
+        jobs[t].status = -2;
+    }
+    for (t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tids[t], NULL, attend_job, &jobs[t]) == 0;
+    attend_job(&jobs[0]);
+    for (t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tids[t], NULL);
+        else
+            attend_job(&jobs[t]);           /* no thread: run it here */
+    }
+    for (t = 0; t < nthreads; ++t)
+        if (jobs[t].status != 0)
+            status = jobs[t].status;
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
+}

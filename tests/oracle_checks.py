@@ -1,0 +1,330 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``check_*`` takes an oracle library handle and raises AssertionError on a
+mismatch.  ``test_oracle.py`` runs them on the real oracle; the mutant test
+runs them on copies of the oracle with a planted mistake and requires that at
+least one check fails for every mutant.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle
+import pagealgos as pa
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TIGHT = 1e-12
+
+
+def _golden(name):
+    return pa.read_golden(os.path.join(GOLDEN, name))
+
+
+def _floats(toks):
+    return [float(t) for t in toks]
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _attn1(lib, q, k, v, **kw):
+    """Single-head oracle call on fp64 [N,d] / [Nk,d] arrays."""
+    O, L = oracle.attention(q[None, None], k[None, None], v[None, None], lib=lib, **kw)
+    return O[0, 0], L[0, 0]
+
+
+def _embed_scores(x):
+    """Q, K, V so that the attention scores are x (scale 1) and O is softmax(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.size
+    d = max(n, 1)
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((n, d)); k[:, 0] = x
+    v = np.eye(n, d)
+    return q, k, v
+
+
+# --------------------------------------------------------------- worked examples
+def check_worked_example(lib):
+    g = _golden("softmax_worked_example.txt")
+    dec = int(g["decimals"][0][0])
+    tol = 0.5 * 10 ** (-dec) + 1e-12
+    x = _floats(g["x"][0])
+    y, m, l = oracle.softmax(x, lib=lib)
+    assert m == float(g["max"][0][0])
+    assert abs(l - float(g["sum"][0][0])) <= tol, l
+    assert np.all(np.abs(y - _floats(g["y"][0])) <= tol), y
+    assert np.all(np.abs(y * l - _floats(g["exponents"][0])) <= tol), y * l
+    # the same numbers through the attention entry: O row = softmax, LSE = m + ln l
+    q, k, v = _embed_scores(x)
+    O, L = _attn1(lib, q, k, v, scale=1.0)
+    assert np.all(np.abs(O[0, :3] - _floats(g["y"][0])) <= tol), O
+    assert abs(math.exp(L[0] - m) - float(g["sum"][0][0])) <= tol, L
+    assert abs(L[0] - (3.0 + math.log(math.exp(-2) + 1 + math.exp(-1)))) <= TIGHT
+
+
+def check_four_element(lib):
+    g = _golden("online_stats_example.txt")
+    x = _floats(g["x"][0])
+    y, m, l = oracle.softmax(x, lib=lib)
+    assert m == float(g["m"][0][0])
+    assert abs(l - float(g["l"][0][0])) <= float(g["page_atol"][0][0])
+    # fp64 rounding of the printed value: the direct sum is ...109 in fp64
+    assert abs(l - float(g["l"][0][0])) <= TIGHT
+    assert np.allclose(np.exp(np.array(x) - m) / l, y, rtol=0, atol=TIGHT)
+    assert np.allclose(y, scipy.special.softmax(x), rtol=0, atol=TIGHT)
+    q, k, v = _embed_scores(x)
+    _, L = _attn1(lib, q, k, v, scale=1.0)
+    assert abs(L[0] - (5.0 + math.log(float(g["l"][0][0])))) <= TIGHT
+
+
+def check_x153(lib):
+    x = [1.0, 5.0, 3.0]
+    y, m, l = oracle.softmax(x, lib=lib)
+    l_closed = math.exp(-4.0) + 1.0 + math.exp(-2.0)
+    assert m == 5.0 and abs(l - l_closed) <= TIGHT
+    mo, lo = pa.online_stats(x)
+    assert mo == m and abs(lo - l) <= TIGHT
+    assert np.allclose(y, [math.exp(-4) / l_closed, 1 / l_closed, math.exp(-2) / l_closed],
+                       rtol=0, atol=TIGHT)
+
+
+# ------------------------------------------------------------------ chunk merge
+def _chunk_matrix():
+    g = _golden("merge_chunking.txt")
+    rows, cols = int(g["rows"][0][0]), int(g["cols"][0][0])
+    X = _rng(1805).standard_normal((rows, cols)) * float(g["sigma"][0][0])
+    r1, npre = (int(t) for t in g["masked_prefix_row"][0])
+    X[r1, :npre] = -np.inf
+    X[int(g["fully_masked_row"][0][0]), :] = -np.inf
+    return X, [int(t) for t in g["chunks"][0]], g
+
+
+def check_chunk_merge(lib):
+    X, widths, g = _chunk_matrix()
+    assert sum(widths) == X.shape[1]
+    full_row = int(g["fully_masked_row"][0][0])
+    for r in range(X.shape[0]):
+        _, m, l = oracle.softmax(X[r], lib=lib)
+        # left fold of chunk statistics
+        mf, lf = pa.tile_stats(X[r], widths)
+        # tree ((c0, c1), (c2, c3)), c4
+        cs, pos = [], 0
+        for w in widths:
+            cs.append(pa.chunk_stats(X[r, pos:pos + w]))
+            pos += w
+        left = pa.merge_ml(*pa.merge_ml(*cs[0], *cs[1]), *pa.merge_ml(*cs[2], *cs[3]))
+        mt, lt = pa.merge_ml(*left, *cs[4])
+        ref = scipy.special.logsumexp(X[r]) if np.isfinite(X[r]).any() else -np.inf
+        assert mf == m and mt == m
+        assert abs(lf - l) <= TIGHT * max(1.0, l) and abs(lt - l) <= TIGHT * max(1.0, l)
+        assert abs(pa.lse_of(m, l) - ref) <= TIGHT or (ref == -np.inf and pa.lse_of(m, l) == -np.inf)
+        assert not math.isnan(l)
+        if r == full_row:
+            assert l == 0.0 and m == -math.inf
+    # the same rows through the attention entry: a masked prefix is, up to key
+    # order, a key length (softmax and LSE do not depend on key order)
+    for r in range(X.shape[0]):
+        fin = X[r][np.isfinite(X[r])]
+        n = X.shape[1]
+        xs = np.concatenate([fin, np.zeros(n - fin.size)])
+        q, k, v = _embed_scores(xs)
+        O, L = oracle.attention(q[None, None], k[None, None], v[None, None], scale=1.0,
+                                key_lens=[fin.size], lib=lib)
+        ref = scipy.special.logsumexp(fin) if fin.size else -np.inf
+        if fin.size:
+            assert abs(L[0, 0, 0] - ref) <= TIGHT
+            assert np.allclose(O[0, 0, 0, :fin.size], scipy.special.softmax(fin), rtol=0, atol=TIGHT)
+        else:
+            assert L[0, 0, 0] == -np.inf and np.all(O == 0) and not np.isnan(O).any()
+
+
+def check_merge_guard_negative_control(lib):
+    # without the guard the fully masked side gives NaN; with it, (m, l) = (-inf, 0)
+    _, m, l = oracle.softmax([-np.inf] * 5, lib=lib)
+    assert m == -np.inf and l == 0.0
+    _, nl = pa.merge_ml_unguarded(m, l, m, l)
+    assert math.isnan(nl)
+    gm, gl = pa.merge_ml(m, l, m, l)
+    assert gm == -np.inf and gl == 0.0
+
+
+# ----------------------------------------------------------------- tiled shapes
+def check_tiled_shapes(lib):
+    g = _golden("tiled_v1_shapes.txt")
+    Br, Bc = int(g["Br"][0][0]), int(g["Bc"][0][0])
+    for idx, sh in enumerate(g["shape"]):
+        N, Nk, d = (int(t) for t in sh)
+        r = _rng(100 + idx)
+        q, k, v = r.standard_normal((N, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+        for causal in (False, True):
+            for kl in (None, max(Nk - 2, 0), 1):
+                O, L = _attn1(lib, q, k, v, causal=causal, key_lens=None if kl is None else [kl])
+                O1, L1 = pa.flash_v1(q, k, v, Br, Bc, causal=causal, kl=kl)
+                O2, L2 = pa.flash_v2(q, k, v, Br, Bc, causal=causal, kl=kl)
+                for Ot, Lt in ((O1, L1), (O2, L2)):
+                    assert np.allclose(O, Ot, rtol=0, atol=TIGHT), (N, Nk, d, causal, kl)
+                    fin = np.isfinite(L)
+                    assert np.array_equal(fin, np.isfinite(Lt))
+                    assert np.allclose(L[fin], Lt[fin], rtol=0, atol=TIGHT)
+        # the library attention (fp64, no mask), as on the page
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None])[0]
+        O, L = _attn1(lib, q, k, v)
+        assert np.allclose(O, ref.numpy(), rtol=0, atol=float(g["page_atol"][0][0]))
+        assert np.allclose(O, ref.numpy(), rtol=0, atol=TIGHT)
+        lse_ref = scipy.special.logsumexp(q @ k.T / math.sqrt(d), axis=1)
+        assert np.allclose(L, lse_ref, rtol=0, atol=TIGHT)
+
+
+# ----------------------------------------------------------------- closed forms
+def check_closed_forms(lib):
+    r = _rng(7)
+    d = 6
+    # one key: O = v0, LSE = s0
+    q, k, v = r.standard_normal((5, d)), r.standard_normal((1, d)), r.standard_normal((1, d))
+    O, L = _attn1(lib, q, k, v, scale=0.7)
+    assert np.allclose(O, np.repeat(v, 5, 0), rtol=0, atol=TIGHT)
+    assert np.allclose(L, 0.7 * (q @ k[0]), rtol=0, atol=TIGHT)
+    # key length 1: O = v0 whatever Nk
+    q, k, v = r.standard_normal((4, d)), r.standard_normal((9, d)), r.standard_normal((9, d))
+    O, L = _attn1(lib, q, k, v, key_lens=[1])
+    assert np.allclose(O, np.repeat(v[:1], 4, 0), rtol=0, atol=TIGHT)
+    # causal, N == Nk: row 0 sees key 0 only; row 1 sees keys 0 and 1
+    q, k, v = r.standard_normal((7, d)), r.standard_normal((7, d)), r.standard_normal((7, d))
+    sc = 1 / math.sqrt(d)
+    O, L = _attn1(lib, q, k, v, causal=True)
+    assert np.allclose(O[0], v[0], rtol=0, atol=TIGHT)
+    assert abs(L[0] - sc * q[0] @ k[0]) <= TIGHT
+    s = sc * (k[:2] @ q[1])
+    w = np.exp(s - s.max()); w /= w.sum()
+    assert np.allclose(O[1], w @ v[:2], rtol=0, atol=TIGHT)
+    # causal with N > Nk: queries are the last N positions, so the first N - Nk rows see nothing
+    q, k, v = r.standard_normal((6, d)), r.standard_normal((4, d)), r.standard_normal((4, d))
+    O, L = _attn1(lib, q, k, v, causal=True)
+    assert np.all(O[:2] == 0) and np.all(L[:2] == -np.inf)
+    assert np.allclose(O[2], v[0], rtol=0, atol=TIGHT)
+    # causal with N < Nk: the last query sees every key
+    q, k, v = r.standard_normal((3, d)), r.standard_normal((8, d)), r.standard_normal((8, d))
+    O, L = _attn1(lib, q, k, v, causal=True)
+    O_full, L_full = _attn1(lib, q[2:], k, v)
+    assert np.allclose(O[2], O_full[0], rtol=0, atol=TIGHT) and abs(L[2] - L_full[0]) <= TIGHT
+    O6, _ = _attn1(lib, q[:1], k[:6], v[:6])
+    assert np.allclose(O[0], O6[0], rtol=0, atol=TIGHT)
+    # zero query: uniform weights over the visible keys
+    q, k, v = np.zeros((3, d)), r.standard_normal((10, d)), r.standard_normal((10, d))
+    O, L = _attn1(lib, q, k, v, key_lens=[7])
+    assert np.allclose(O, np.repeat(v[:7].mean(0, keepdims=True), 3, 0), rtol=0, atol=TIGHT)
+    assert np.allclose(L, math.log(7), rtol=0, atol=TIGHT)
+    # identical keys: uniform weights, LSE = s + ln Nk
+    q, k1, v = r.standard_normal((2, d)), r.standard_normal((1, d)), r.standard_normal((5, d))
+    k = np.repeat(k1, 5, 0)
+    O, L = _attn1(lib, q, k, v)
+    assert np.allclose(O, np.repeat(v.mean(0, keepdims=True), 2, 0), rtol=0, atol=TIGHT)
+    assert np.allclose(L, sc * (q @ k1[0]) + math.log(5), rtol=0, atol=TIGHT)
+    # identity values (d >= Nk): the output row is the probability row
+    q, k = r.standard_normal((4, 8)), r.standard_normal((5, 8))
+    v = np.eye(5, 8)
+    O, L = _attn1(lib, q, k, v, scale=0.3)
+    P = scipy.special.softmax(0.3 * q @ k.T, axis=1)
+    assert np.allclose(O[:, :5], P, rtol=0, atol=TIGHT) and np.all(O[:, 5:] == 0)
+    # no keys at all: every row fully masked
+    O, L = oracle.attention(np.ones((1, 2, 3, 4)), np.ones((1, 2, 0, 4)), np.ones((1, 2, 0, 4)), lib=lib)
+    assert np.all(O == 0) and np.all(L == -np.inf)
+    # key length 0 on one batch only
+    q, k, v = r.standard_normal((2, 1, 3, d)), r.standard_normal((2, 1, 4, d)), r.standard_normal((2, 1, 4, d))
+    O, L = oracle.attention(q, k, v, key_lens=[4, 0], lib=lib)
+    assert np.all(O[1] == 0) and np.all(L[1] == -np.inf) and np.all(np.isfinite(L[0]))
+
+
+# ------------------------------------------------------------------- invariants
+def check_invariants(lib):
+    r = _rng(11)
+    N, Nk, d = 5, 9, 7
+    q, k, v = r.standard_normal((N, d)), r.standard_normal((Nk, d)), r.standard_normal((Nk, d))
+    O, L = _attn1(lib, q, k, v)
+    perm = r.permutation(Nk)
+    Op, Lp = _attn1(lib, q, k[perm], v[perm])
+    assert np.allclose(O, Op, rtol=0, atol=TIGHT) and np.allclose(L, Lp, rtol=0, atol=TIGHT)
+    # convex combination of the value rows
+    assert np.all(O <= v.max(0) + TIGHT) and np.all(O >= v.min(0) - TIGHT)
+    # LSE >= max score, LSE <= max score + ln Nk
+    s = q @ k.T / math.sqrt(d)
+    assert np.all(L >= s.max(1) - TIGHT) and np.all(L <= s.max(1) + math.log(Nk) + TIGHT)
+    # every key twice: same output, LSE + ln 2
+    O2, L2 = _attn1(lib, q, np.concatenate([k, k]), np.concatenate([v, v]))
+    assert np.allclose(O, O2, rtol=0, atol=TIGHT) and np.allclose(L + math.log(2), L2, rtol=0, atol=TIGHT)
+    # adding a constant vector to V adds it to O (weights sum to 1)
+    c = r.standard_normal(d)
+    O3, _ = _attn1(lib, q, k, v + c)
+    assert np.allclose(O3, O + c, rtol=0, atol=1e-11)
+
+
+def check_torch_sdpa(lib):
+    r = _rng(23)
+    B, H, N, Nk, d = 2, 3, 7, 11, 5
+    q, k, v = (r.standard_normal(s) for s in ((B, H, N, d), (B, H, Nk, d), (B, H, Nk, d)))
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    O, L = oracle.attention(q, k, v, lib=lib)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    assert np.allclose(O, ref.numpy(), rtol=0, atol=TIGHT)
+    lse = torch.logsumexp(torch.matmul(tq, tk.transpose(-1, -2).contiguous()) / math.sqrt(d), dim=-1)
+    assert np.allclose(L, lse.numpy(), rtol=0, atol=TIGHT)
+    # causal, N == Nk (the library aligns the mask at the top-left; equal here)
+    q2, k2, v2 = q[:, :, :6], k[:, :, :6], v[:, :, :6]
+    O, L = oracle.attention(q2, k2, v2, causal=True, lib=lib)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q2), torch.from_numpy(k2), torch.from_numpy(v2), is_causal=True)
+    assert np.allclose(O, ref.numpy(), rtol=0, atol=TIGHT)
+    # causal, N < Nk: bottom-right alignment as an explicit boolean mask
+    mask = np.arange(Nk)[None, :] <= np.arange(N)[:, None] + (Nk - N)
+    O, L = oracle.attention(q, k, v, causal=True, lib=lib)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask))
+    assert np.allclose(O, ref.numpy(), rtol=0, atol=TIGHT)
+
+
+def check_bf16_widening(lib):
+    g = torch.Generator().manual_seed(5)
+    q = (torch.randn(1, 2, 5, 8, generator=g) * 3).to(torch.bfloat16)
+    k = torch.randn(1, 2, 6, 8, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 2, 6, 8, generator=g).to(torch.bfloat16)
+    Ob, Lb = oracle.attention(q, k, v, causal=True, lib=lib)
+    Od, Ld = oracle.attention(q.double(), k.double(), v.double(), causal=True, lib=lib)
+    assert np.array_equal(Ob, Od) and np.array_equal(Lb, Ld)
+    Of, Lf = oracle.attention(q.float(), k.float(), v.float(), causal=True, lib=lib)
+    assert np.array_equal(Of, Od) and np.array_equal(Lf, Ld)
+
+
+def check_rows_and_threads(lib):
+    r = _rng(31)
+    B, H, N, Nk, d = 2, 2, 9, 13, 4
+    q, k, v = (r.standard_normal(s) for s in ((B, H, N, d), (B, H, Nk, d), (B, H, Nk, d)))
+    O, L = oracle.attention(q, k, v, causal=True, key_lens=[10, 3], nthreads=1, lib=lib)
+    O8, L8 = oracle.attention(q, k, v, causal=True, key_lens=[10, 3], nthreads=8, lib=lib)
+    assert np.array_equal(O, O8) and np.array_equal(L, L8)
+    rows = [0, 5, 17, 20, 35, 2 * 2 * 9 - 1]
+    Or, Lr = oracle.attention(q, k, v, causal=True, key_lens=[10, 3], rows=rows, lib=lib)
+    assert np.array_equal(Or, O.reshape(-1, d)[rows]) and np.array_equal(Lr, L.reshape(-1)[rows])
+    # key length k equals truncating K and V to their first k rows
+    for b, kl in enumerate([10, 3]):
+        Ot, Lt = oracle.attention(q[b:b + 1], k[b:b + 1, :, :kl], v[b:b + 1, :, :kl], lib=lib)
+        Ok, Lk = oracle.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], key_lens=[kl], lib=lib)
+        assert np.array_equal(Ot, Ok) and np.array_equal(Lt, Lk)
+    # per-batch key lengths index the batch, not the head
+    Ob, Lb = oracle.attention(q, k, v, key_lens=[13, 2], lib=lib)
+    O0, L0 = oracle.attention(q[:1], k[:1], v[:1], lib=lib)
+    O1, L1 = oracle.attention(q[1:], k[1:, :, :2], v[1:, :, :2], lib=lib)
+    assert np.array_equal(Ob[0], O0[0]) and np.array_equal(Ob[1], O1[0])
+
+
+ALL_CHECKS = [
+    check_worked_example, check_four_element, check_x153, check_chunk_merge,
+    check_merge_guard_negative_control, check_tiled_shapes, check_closed_forms,
+    check_invariants, check_torch_sdpa, check_bf16_widening, check_rows_and_threads,
+]

@@ -1,0 +1,53 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle.c with one plausible slip (a dropped term, a
+wrong sign or index, a swapped operand) compiled on the CPU; the pin suite is
+then run against it.  This checks the pins, not the product.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "dropped_scale": ("s[j] = a->scale * dot;", "s[j] = dot;"),
+    "no_max_shift_in_sum": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
+    "wrong_sign_in_exp": ("double p = exp(s[j] - m) / l;", "double p = exp(m - s[j]) / l;"),
+    "no_divide": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
+    "lse_drops_max": ("a->LSE[out_row] = m + log(l);", "a->LSE[out_row] = log(l);"),
+    "causal_off_by_one": ("long lim = i + (a->Nk - a->N) + 1;", "long lim = i + (a->Nk - a->N);"),
+    "causal_top_left": ("long lim = i + (a->Nk - a->N) + 1;", "long lim = i + 1;"),
+    "key_len_by_head": ("nvis = visible_keys(a, b, i);", "nvis = visible_keys(a, bh % a->B, i);"),
+    "k_swapped_for_v": ("* widen(a->K, a->dtype, kvoff + (size_t)j * d + c);",
+                        "* widen(a->V, a->dtype, kvoff + (size_t)j * d + c);"),
+    "bf16_shift": ("(uint32_t)((const uint16_t *)base)[idx] << 16;",
+                   "(uint32_t)((const uint16_t *)base)[idx] << 15;"),
+    "softmax_no_shift": ("y[j] = exp(x[j] - m) / l;", "y[j] = exp(x[j]) / l;"),
+    "softmax_min_not_max": ("if (x[j] > m)\n            m = x[j];", "if (x[j] > m && m == -INFINITY)\n            m = x[j];"),
+    "masked_row_lse_zero": ("a->LSE[out_row] = -INFINITY;\n        return;", "a->LSE[out_row] = 0.0;\n        return;"),
+    "row_index_swapped": ("long bh = flat / a->N, i = flat % a->N, b = bh / a->H;",
+                          "long bh = flat / a->N, i = flat % a->N, b = bh % a->B;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    find, repl = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site for {name} not unique/found"
+    mpath = tmp_path / "oracle_mutant.c"
+    mpath.write_text(src.replace(find, repl))
+    so = str(tmp_path / f"liboracle_{name}.so")
+    oracle.build(so, str(mpath))
+    lib = oracle.load(so, rebuild_if_missing=False)
+    failed = []
+    for check in oc.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, RuntimeError, ValueError, FloatingPointError):
+            failed.append(check.__name__)
+    assert failed, f"no pin caught mutant {name}"
