@@ -1,0 +1,12 @@
+"""MI355X (gfx950) fused attention forward with the online-softmax recurrence.
+
+The computation lives in libfa.so (hand-written HIP kernels behind the C ABI of
+include/fa.h); this package only marshals torch tensors into that ABI.
+"""
+from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_F32,
+                 FA_OK, FaError, attention, decode, fa_decode_splitkv, fa_decode_workspace_bytes,
+                 fa_forward, load_library, status_str)
+
+__all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_F32",
+           "FA_OK", "FaError", "attention", "decode", "fa_decode_splitkv",
+           "fa_decode_workspace_bytes", "fa_forward", "load_library", "status_str"]

@@ -1,0 +1,105 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: argument checks, kernel
+// selection and launch-error reporting.  Every check happens on the host
+// before any launch; nothing here allocates device memory.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+fa_status from_hip(hipError_t e) {
+    if (e == hipSuccess) return FA_OK;
+    std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
+                  hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
+
+constexpr long long kMaxGridX = 0x7fffffffLL;
+constexpr long long kMaxGridYZ = 65535;
+constexpr long long kMaxElems = 1LL << 46;   // far beyond 288 GB of bf16
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_str(fa_status status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char *fa_last_hip_error(void) { return g_last_hip_error; }
+
+fa_status fa_forward(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                     int H, int N, int Nk, int d, float scale, int causal,
+                     const int32_t *key_lens, fa_dtype dtype, void *stream) {
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_F32 && d > 256) return FA_ERR_UNSUPPORTED;
+    if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
+    const long long rows = (long long)B * H * N;
+    if (rows == 0) return FA_OK;
+    if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if (!Q || !O || !LSE) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE)) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!aligned16(K) || !aligned16(V))) return FA_ERR_INVALID_ARG;
+    if (key_lens && !aligned4(key_lens)) return FA_ERR_INVALID_ARG;
+    const int rows_per_block = dtype == FA_BF16 ? 128 : 64;
+    const long long nblocks = (long long)B * H * ((N + rows_per_block - 1) / rows_per_block);
+    if (nblocks > kMaxGridX) return FA_ERR_INVALID_ARG;
+
+    fa::FwdArgs a{Q, K, V, O, LSE, key_lens, B, H, N, Nk, d, scale, causal};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
+    if (B < 0 || H < 0 || d < 0 || num_splits < 1) return 0;
+    return (size_t)B * (size_t)H * (size_t)num_splits * ((size_t)d + 2) * sizeof(float);
+}
+
+fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                            int B, int H, int Nk, int d, float scale, const int32_t *key_lens,
+                            int num_splits, void *workspace, size_t workspace_bytes,
+                            fa_dtype dtype, void *stream) {
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (num_splits > 256) return FA_ERR_UNSUPPORTED;
+    if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA_OK;
+    if ((long long)B * H * (long long)Nk * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if (B > kMaxGridYZ || H > kMaxGridYZ || (long long)B * H > kMaxGridX) return FA_ERR_INVALID_ARG;
+    if (!Q || !O || !LSE || !workspace) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE) || !aligned16(workspace))
+        return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!aligned16(K) || !aligned16(V))) return FA_ERR_INVALID_ARG;
+    if (key_lens && !aligned4(key_lens)) return FA_ERR_INVALID_ARG;
+    if (workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_INVALID_ARG;
+
+    fa::DecodeArgs a{Q, K, V, O, LSE, key_lens, B, H, Nk, d, scale, num_splits,
+                     static_cast<float *>(workspace)};
+    return from_hip(fa::launch_decode(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

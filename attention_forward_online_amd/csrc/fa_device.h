@@ -1,0 +1,51 @@
+// fa_device.h -- device-side helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// 2^x and log2(x) on the transcendental unit (v_exp_f32 / v_log_f32).
+// exp(x) is evaluated as 2^(x * log2 e); the log2(e) factor is folded into
+// the score scale once per launch.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Two floats to two bf16 (round to nearest even, v_cvt_pk_bf16_f32), packed lo|hi.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Value of lane (lane ^ mask) for masks < 64.
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+// Even split of a clamped key length: the visible keys of batch b.
+__device__ __forceinline__ int visible_len(const int32_t *key_lens, int b, int Nk) {
+    if (!key_lens) return Nk;
+    int kl = key_lens[b];
+    return kl < 0 ? 0 : (kl > Nk ? Nk : kl);
+}
+
+}  // namespace fa

@@ -1,0 +1,39 @@
+// fa_kernels.h -- host-side launch interface between the C ABI layer and the
+// gfx950 kernels.  Arguments reaching these functions have already been
+// validated by fa_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *Q, *K, *V;
+    void *O;
+    float *LSE;
+    const int32_t *key_lens;    // device int32[B] or nullptr
+    int B, H, N, Nk, d;
+    float scale;                // > 0, finite
+    int causal;                 // 0 or 1
+};
+
+struct DecodeArgs {
+    const void *Q, *K, *V;
+    void *O;
+    float *LSE;
+    const int32_t *key_lens;
+    int B, H, Nk, d;
+    float scale;
+    int num_splits;
+    float *workspace;           // B*H*num_splits*(d+2) floats
+};
+
+// bf16 prefill, d in {64, 128}: MFMA 32x32x16 bf16 tiles.
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
+// fp32 prefill, 1 <= d <= 256: fp32 FMA tiles.
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
+// split-KV decode, d in {64, 128}; is_bf16 selects the element type.
+hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,177 @@
+"""Python binding of the C ABI in include/fa.h (argument marshalling only).
+
+Each function passes device pointers of torch tensors, their sizes and torch's
+current HIP stream to the same-named entry point of libfa.so; every step of the
+computation runs in the library's kernels.  There is no fallback: if libfa.so
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_BF16 = 0, 1
+
+#: every symbol include/fa.h declares
+EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_str",
+           "fa_last_hip_error")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = status_str(status) if _lib is not None else str(status)
+        super().__init__(f"{where}: {name}{(' (' + detail + ')') if detail else ''}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so and declare the ABI.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m attention_forward_online_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, i, vp, sz, i, vp]
+    lib.fa_decode_splitkv.restype = i
+    lib.fa_status_str.argtypes = [i]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_last_hip_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+               lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+               key_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+    """O, LSE <- attention(q, k, v) through the C entry point fa_forward.
+
+    q, o: [B,H,N,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,N]; key_lens: int32 [B] or None.
+    """
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
+            or lse.shape != (B, H, N):
+        raise ValueError("shape mismatch between q, k, v, o and lse")
+    if key_lens is not None:
+        _check_dev("key_lens", key_lens, torch.int32)
+        if key_lens.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    st = lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
+                        float(scale), int(bool(causal)), _ptr(key_lens), _dtype_code(q),
+                        _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_forward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                      lse: torch.Tensor, num_splits: int, workspace: torch.Tensor,
+                      scale: Optional[float] = None, key_lens: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """One-query split-KV decode through the C entry point fa_decode_splitkv.
+
+    q, o: [B,H,1,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,1]; workspace: a GPU
+    tensor of at least fa_decode_workspace_bytes(B, H, d, num_splits) bytes.
+    """
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if N != 1 or k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
+            or lse.shape != (B, H, 1):
+        raise ValueError("decode expects q, o [B,H,1,d], k, v [B,H,Nk,d], lse [B,H,1]")
+    if key_lens is not None:
+        _check_dev("key_lens", key_lens, torch.int32)
+        if key_lens.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d,
+                               float(scale), _ptr(key_lens), int(num_splits), _ptr(workspace),
+                               ws_bytes, _dtype_code(q), _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_splitkv",
+                      lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def attention(q, k, v, scale=None, causal=False, key_lens=None):
+    """Allocate O and LSE, run fa_forward, return (O, LSE)."""
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_forward(q, k, v, o, lse, scale=scale, causal=causal, key_lens=key_lens)
+    return o, lse
+
+
+def decode(q, k, v, num_splits=16, scale=None, key_lens=None):
+    """Allocate O, LSE and the workspace, run fa_decode_splitkv, return (O, LSE)."""
+    B, H, _, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_bytes(B, H, d, num_splits)
+    ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    fa_decode_splitkv(q, k, v, o, lse, num_splits, ws, scale=scale, key_lens=key_lens)
+    return o, lse

@@ -1,0 +1,240 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one fa_forward call on the causal prefill workload
+B=4 H=16 N=Nk=2048 d=64 bf16 (fp32 accumulation); its inputs are resident in
+device memory before timing starts.  The headline value is TFLOP/s with
+4*B*H*N*Nk*d FLOPs halved for causal (QK^T and PV only).  The same run also
+times the split-KV decode (B=64 H=32, Nk=16384, d=128, 16 splits) in HBM GB/s
+and the other prefill workloads, and times the fp64 CPU oracle on the host's
+cores on the headline workload as a reported baseline.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "fused attention fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB/s"
+HEADLINE = "causal_bf16_b4h16_n2048_d64"
+DECODE = "decode_bf16_b64h32_nk16384_d128"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def prefill_flops(w, key_lens=None):
+    """4*B*H*N*Nk*d (halved for causal); with key lengths the visible count."""
+    if key_lens is not None:
+        return 4.0 * w.H * w.N * w.d * float(sum(min(max(k, 0), w.Nk) for k in key_lens))
+    f = 4.0 * w.B * w.H * w.N * w.Nk * w.d
+    return f / 2 if w.causal else f
+
+
+def decode_bytes(w):
+    """Compulsory HBM bytes of one decode call: K, V, Q read; O, LSE written."""
+    el = 2 if w.dtype == "bf16" else 4
+    return (2 * w.B * w.H * w.Nk * w.d + 2 * w.B * w.H * w.d) * el + w.B * w.H * 4
+
+
+def time_launches(fn, steps, warmup):
+    """Per-launch HIP event times (ms) on torch's current stream, which is the
+    stream the library launches on; also the total over the timed region."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return per, t0.elapsed_time(t1)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_forward_online_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernels changed after the counters were taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    rec = t.get(kernel_key)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time only the headline prefill (used under the profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(every workload here is measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_forward_online_amd as fa
+    from attention_forward_online_amd import build as fabuild
+    from attention_forward_online_amd.synth import WORKLOADS, make_inputs
+
+    if not os.path.exists(fabuild.LIB_PATH):
+        fabuild.build()
+    fa.load_library()
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    # ---------------------------------------------------------------- headline
+    w = WORKLOADS[HEADLINE]
+    inp = make_inputs(w, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
+    per, total = time_launches(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
+                               args.steps, args.warmup)
+    flops = prefill_flops(w)
+    ms_step = total / args.steps
+    avg_launch = float(np.mean(per))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch * 1e-3) / 1e12
+    traffic = measured_traffic("fwd_bf16_kernel<64,true>/" + HEADLINE)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) bf16 Q, K, V drawn on the device",
+        "config": {"workload": w.describe(), "name": HEADLINE, "B": w.B, "H": w.H, "N": w.N,
+                   "Nk": w.Nk, "d": w.d, "causal": True, "scale": w.scale,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64,true>",
+                     "avg_launch_ms": round(avg_launch, 5)},
+    }
+    head_out = (o, lse)
+
+    if not args.only_headline:
+        # ------------------------------------------------------------ decode
+        wd = WORKLOADS[DECODE]
+        di = make_inputs(wd, device=dev)
+        od = torch.empty_like(di["q"])
+        ld = torch.empty(wd.B, wd.H, 1, device=dev, dtype=torch.float32)
+        nb = fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits)
+        ws = torch.empty(nb // 4, device=dev, dtype=torch.float32)
+        dsteps = max(5, args.steps // 5)
+        per_d, tot_d = time_launches(
+            lambda: fa.fa_decode_splitkv(di["q"], di["k"], di["v"], od, ld, wd.num_splits, ws),
+            dsteps, max(2, args.warmup // 2))
+        nbytes = decode_bytes(wd)
+        ms_d = tot_d / dsteps
+        gbs = nbytes / (ms_d * 1e-3) / 1e9
+        gbs_launch = nbytes / (float(np.mean(per_d)) * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": wd.describe(), "name": DECODE, "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_call": round(ms_d, 4), "bytes_per_call": nbytes,
+            "workspace_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs_launch, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs_launch / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode/" + DECODE),
+                         "kernels": "decode_split_kernel + decode_combine_kernel"},
+        }
+        del di, od, ld, ws
+        torch.cuda.empty_cache()
+
+        # ------------------------------------------------- other prefill shapes
+        others = {}
+        for name in ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",
+                     "tiny_f32_b1h1_n256_d64"):
+            wo = WORKLOADS[name]
+            oi = make_inputs(wo, device=dev)
+            oo = torch.empty_like(oi["q"])
+            ol = torch.empty(wo.B, wo.H, wo.N, device=dev, dtype=torch.float32)
+            kl = oi["key_lens"]
+            st = max(5, args.steps // 5)
+            per_o, tot_o = time_launches(
+                lambda: fa.fa_forward(oi["q"], oi["k"], oi["v"], oo, ol, causal=wo.causal,
+                                      key_lens=kl), st, 3)
+            ms_o = float(np.mean(per_o))
+            nominal = prefill_flops(wo)
+            rec = {"workload": wo.describe(), "ms_per_call": round(ms_o, 5),
+                   "tflops_nominal": round(nominal / (ms_o * 1e-3) / 1e12, 2)}
+            peak = PEAK_F32_TFLOPS if wo.dtype == "f32" else PEAK_BF16_TFLOPS
+            if kl is not None:
+                eff = prefill_flops(wo, kl.tolist())
+                rec["key_lens"] = kl.tolist()
+                rec["tflops_effective"] = round(eff / (ms_o * 1e-3) / 1e12, 2)
+                rec["frac_effective"] = round(eff / (ms_o * 1e-3) / 1e12 / peak, 4)
+            else:
+                rec["frac"] = round(nominal / (ms_o * 1e-3) / 1e12 / peak, 4)
+            rec["peak"] = peak
+            others[name] = rec
+            del oi, oo, ol
+        out["workloads"] = others
+
+    # ------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+        t = time.perf_counter()
+        O_ref, L_ref = oracle.attention(qh, kh, vh, scale=float(np.float32(w.scale)), causal=True,
+                                        nthreads=nthreads)
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": nthreads, "kind": "oracle",
+                               "sample": f"the whole headline workload ({HEADLINE}), one fp64 pass, "
+                                         f"{dt:.2f} s wall"}
+        # the oracle's outputs double as a full parity check of the timed run
+        og = head_out[0].double().cpu().numpy()
+        lg = head_out[1].double().cpu().numpy()
+        out["parity"] = {"max_abs_O": float(np.abs(og - O_ref).max()),
+                         "max_abs_LSE": float(np.abs(lg - L_ref).max()),
+                         "tolerance": {"O": 2e-2, "LSE": 1e-3}}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The library computes O = softmax(scale * Q K^T) V and the row log-sum-exp
+ * LSE = ln sum_j exp(scale * q . k_j) with the online-softmax recurrence: a
+ * running max m, a running denominator l and an unnormalised output o per query
+ * row are updated key tile by key tile, the old state is rescaled by
+ * exp(m_old - m_new) when the max grows, and the result is o / l
+ * ('Online Softmax -- the mathematical heart of FlashAttention', sections 4-5;
+ * 'Online Softmax' (research-hub concept page), "Key math").  The N x Nk score
+ * matrix never reaches device memory.
+ *
+ * Conventions shared by every entry point
+ *   Memory     All tensor pointers are DEVICE pointers, row-major, contiguous:
+ *              Q, O [B, H, N, d]; K, V [B, H, Nk, d]; LSE [B, H, N] (fp32).
+ *              Q, K, V and O must be 16-byte aligned.
+ *   Ownership  The caller allocates and owns every buffer; the library
+ *              allocates nothing and keeps no pointer after a call returns.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *              are asynchronous on that stream; the status only reports
+ *              argument checks and launch errors.  Calls are reentrant.
+ *   Masking    key_lens (device int32[B] or NULL): keys j >= key_lens[b] are
+ *              invisible to every query of batch b; values outside [0, Nk] are
+ *              clamped on the device.  causal = 1 hides key j from query i when
+ *              j > i + (Nk - N) (queries are the last N positions; j > i when
+ *              N == Nk).  The two combine by AND.
+ *   Empty rows A query row with no visible key gets O = 0 and LSE = -inf,
+ *              never NaN ('Online Softmax & FlashAttention' (interview lesson),
+ *              Step 1: the fully masked row keeps m = -inf, l = 0).
+ *   Errors     Every argument is checked on the host before any launch; on an
+ *              error nothing is launched.  The library never aborts.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, negative size, bad flag, too-small workspace */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request this build has no kernel for (e.g. bf16 with d = 96) */
+    FA_ERR_HIP = 3            /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum fa_dtype {
+    FA_F32 = 0,               /* Q, K, V, O are fp32; fp32 arithmetic throughout */
+    FA_BF16 = 1               /* Q, K, V, O are bf16; fp32 accumulation, bf16 MFMA operands */
+} fa_dtype;
+
+/*
+ * Prefill attention forward.
+ *   Computes, for every b < B, h < H, i < N:
+ *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
+ *     LSE[b,h,i] = ln sum_j exp(scale * Q[b,h,i,:] . K[b,h,j,:])
+ *   over the keys j visible to (b, i) (see Masking), one Q tile per
+ *   workgroup, K/V tiles streamed through LDS ('Online Softmax &
+ *   FlashAttention', Step 3: the outer loop runs over independent Q blocks,
+ *   the inner one over K/V; Step 4: causal tiles above the diagonal are
+ *   skipped, tiles on it are masked).
+ *   Q, K, V, O: element type `dtype`; LSE: fp32.
+ *   scale: finite and > 0 (usually 1/sqrt(d)); scale <= 0 gives
+ *   FA_ERR_UNSUPPORTED, a non-finite scale FA_ERR_INVALID_ARG.
+ *   causal: 0 or 1.  key_lens: device int32[B] or NULL.
+ *   Supported: FA_BF16 with d in {64, 128}; FA_F32 with 1 <= d <= 256.
+ *   B*H*N == 0: nothing to do, FA_OK.  Nk == 0: every row fully masked.
+ */
+fa_status fa_forward(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                     int B, int H, int N, int Nk, int d, float scale, int causal,
+                     const int32_t *key_lens, fa_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace fa_decode_splitkv needs:
+ * B * H * num_splits * (d + 2) * 4 (a running max, a denominator and an
+ * unnormalised output row in fp32 for every split).  Returns 0 for negative
+ * arguments or num_splits < 1.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * One-query decode with the key range split into chunks (Flash-Decoding,
+ * 'Online Softmax & FlashAttention', Step 5).
+ *   Q, O: [B, H, 1, d]; K, V: [B, H, Nk, d]; LSE: [B, H, 1] fp32.
+ *   The visible keys [0, kl) of batch b, kl = clamp(key_lens[b], 0, Nk) (Nk
+ *   when key_lens is NULL), are cut into num_splits consecutive chunks of
+ *   ceil(kl / num_splits) keys (trailing chunks may be short or empty).  One
+ *   pass computes each chunk's partial state (m_c, l_c, o_c); a second pass
+ *   merges the partials with the associative (m, l) merge
+ *   m = max(m1, m2), l = exp(m1 - m) l1 + exp(m2 - m) l2 (o alike), where two
+ *   -inf sides merge to (-inf, 0) ('Online Softmax & FlashAttention', Step 1),
+ *   and writes O = o / l and LSE = m + ln l.  The result equals fa_forward
+ *   with N = 1 and causal = 0 up to rounding.
+ *   workspace: device memory of at least fa_decode_workspace_bytes(B, H, d,
+ *   num_splits) bytes, 16-byte aligned, owned by the caller; its contents on
+ *   entry do not matter and are overwritten.  Two calls that share a
+ *   workspace must not overlap in time (same stream, or synchronised).
+ *   Supported: FA_BF16 and FA_F32 with d in {64, 128}; 1 <= num_splits <= 256.
+ */
+fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                            int B, int H, int Nk, int d, float scale,
+                            const int32_t *key_lens, int num_splits,
+                            void *workspace, size_t workspace_bytes,
+                            fa_dtype dtype, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fa_status_str(fa_status status);
+
+/* Text of the last HIP error this thread's calls saw ("" if none). */
+const char *fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports what include/fa.h declares,
+and rejects bad arguments before launching anything (no GPU is touched: every
+call here returns from the host-side checks)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_forward_online_amd as fa
+from attention_forward_online_amd import build as fabuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# fake, 16-byte aligned, never dereferenced: every call below fails validation
+P = 0x10000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fabuild.LIB_PATH):
+        fabuild.build()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fabuild.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    assert fa.status_str(fa.FA_OK) == "FA_OK"
+    assert fa.status_str(fa.FA_ERR_INVALID_ARG) == "FA_ERR_INVALID_ARG"
+    assert fa.status_str(fa.FA_ERR_UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.status_str(fa.FA_ERR_HIP) == "FA_ERR_HIP"
+    assert fa.status_str(99) == "FA_ERR_UNKNOWN"
+    assert lib.fa_last_hip_error() == b""
+
+
+def fwd(lib, Q=P, K=P, V=P, O=P, LSE=P, B=1, H=1, N=4, Nk=4, d=64, scale=0.125, causal=0,
+        key_lens=None, dtype=fa.FA_BF16):
+    return lib.fa_forward(Q, K, V, O, LSE, B, H, N, Nk, d, scale, causal, key_lens, dtype, None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    bad = fa.FA_ERR_INVALID_ARG
+    assert fwd(lib, dtype=7) == bad
+    assert fwd(lib, B=-1) == bad and fwd(lib, H=-1) == bad
+    assert fwd(lib, N=-1) == bad and fwd(lib, Nk=-1) == bad
+    assert fwd(lib, d=0) == bad and fwd(lib, d=-64) == bad
+    assert fwd(lib, causal=2) == bad
+    assert fwd(lib, scale=float("nan")) == bad and fwd(lib, scale=float("inf")) == bad
+    assert fwd(lib, Q=None) == bad and fwd(lib, O=None) == bad and fwd(lib, LSE=None) == bad
+    assert fwd(lib, K=None) == bad and fwd(lib, V=None) == bad
+    assert fwd(lib, Q=P + 2) == bad and fwd(lib, O=P + 8) == bad and fwd(lib, K=P + 4) == bad
+    assert fwd(lib, LSE=P + 2) == bad
+    assert fwd(lib, key_lens=P + 1) == bad
+    # grid beyond the hardware limit
+    assert fwd(lib, B=65536, H=65536, N=128, d=64) == bad
+
+
+def test_forward_unsupported_is_explicit(lib):
+    uns = fa.FA_ERR_UNSUPPORTED
+    for d in (32, 96, 80, 256):
+        assert fwd(lib, d=d, dtype=fa.FA_BF16) == uns
+    assert fwd(lib, d=257, dtype=fa.FA_F32) == uns
+    assert fwd(lib, scale=0.0) == uns and fwd(lib, scale=-0.5) == uns
+
+
+def test_forward_empty_is_a_noop(lib):
+    # nothing to compute: returns before any pointer is looked at
+    assert fwd(lib, Q=None, K=None, V=None, O=None, LSE=None, B=0) == fa.FA_OK
+    assert fwd(lib, Q=None, K=None, V=None, O=None, LSE=None, H=0) == fa.FA_OK
+    assert fwd(lib, Q=None, K=None, V=None, O=None, LSE=None, N=0) == fa.FA_OK
+
+
+def test_workspace_bytes(lib):
+    assert fa.fa_decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 1) == 66 * 4
+    assert fa.fa_decode_workspace_bytes(-1, 1, 64, 1) == 0
+    assert fa.fa_decode_workspace_bytes(1, 1, 64, 0) == 0
+
+
+def dec(lib, Q=P, K=P, V=P, O=P, LSE=P, B=2, H=2, Nk=64, d=128, scale=0.1, key_lens=None,
+        S=4, ws=P, ws_bytes=None, dtype=fa.FA_BF16):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_bytes(B, H, d, S)
+    return lib.fa_decode_splitkv(Q, K, V, O, LSE, B, H, Nk, d, scale, key_lens, S, ws, ws_bytes,
+                                 dtype, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    bad, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    assert dec(lib, dtype=3) == bad
+    assert dec(lib, S=0, ws_bytes=1 << 20) == bad
+    assert dec(lib, ws=None) == bad
+    assert dec(lib, ws_bytes=10) == bad
+    assert dec(lib, ws_bytes=lib.fa_decode_workspace_bytes(2, 2, 128, 4) - 4) == bad
+    assert dec(lib, ws=P + 4) == bad
+    assert dec(lib, Q=None) == bad and dec(lib, K=None) == bad and dec(lib, LSE=None) == bad
+    assert dec(lib, Nk=-1) == bad and dec(lib, d=0) == bad
+    assert dec(lib, scale=float("nan")) == bad
+    assert dec(lib, B=70000, ws_bytes=1 << 40) == bad
+    assert dec(lib, d=96) == uns and dec(lib, d=256) == uns
+    assert dec(lib, S=257, ws_bytes=1 << 30) == uns
+    assert dec(lib, scale=0.0) == uns
+    assert dec(lib, Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == fa.FA_OK
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        fa.load_library(str(tmp_path / "libfa.so"))

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Tolerances (max |GPU - oracle|): fp32 1e-5 on O and LSE;
+bf16 2e-2 on O and 1e-3 on LSE.  Rows without a visible key must be exactly
+O = 0, LSE = -inf; no NaN anywhere."""
+import numpy as np
+import pytest
+import torch
+
+import attention_forward_online_amd as fa
+import oracle
+from attention_forward_online_amd.synth import WORKLOADS, make_inputs, random_case
+from gpu_common import compare, forward_and_check, sample_rows, say, to_host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+F32, BF16 = torch.float32, torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    fa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ fp32 path
+def test_f32_tiny_workload():
+    w = WORKLOADS["tiny_f32_b1h1_n256_d64"]
+    inp = make_inputs(w, device=DEV)
+    eo, el, *_ = forward_and_check(inp, w.causal, what=w.name)
+    say(f"    max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+
+
+@pytest.mark.parametrize("N,Nk,d", [(6, 6, 4), (10, 7, 8), (1, 1, 2), (5, 13, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_page_tile_shapes(N, Nk, d, causal):
+    inp = random_case(1, 1, N, Nk, d, F32, seed=3, device=DEV)
+    forward_and_check(inp, causal, what="page shape")
+
+
+@pytest.mark.parametrize("d", [1, 3, 16, 17, 64, 100, 128, 200, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_head_dims_ragged(d, causal):
+    inp = random_case(2, 2, 70, 97, d, F32, seed=d, device=DEV, key_lens=[50, 97])
+    forward_and_check(inp, causal, what="f32 ragged")
+
+
+def test_f32_key_lens_edges():
+    inp = random_case(5, 1, 40, 33, 32, F32, seed=9, device=DEV, key_lens=[0, 1, 32, 33, 1000])
+    forward_and_check(inp, False, what="f32 key_lens")
+    inp["key_lens"] = torch.tensor([-5, 2, 31, 7, 0], dtype=torch.int32, device=DEV)
+    forward_and_check(inp, True, what="f32 key_lens causal")
+
+
+# ------------------------------------------------------------------ bf16 prefill
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,Nk", [(300, 333), (128, 128), (1, 1), (1, 200), (200, 390), (390, 200),
+                                  (257, 64), (64, 1)])
+def test_bf16_ragged(d, causal, N, Nk):
+    inp = random_case(2, 3, N, Nk, d, BF16, seed=N + Nk, device=DEV)
+    forward_and_check(inp, causal, what="bf16 ragged")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_key_lens(d, causal):
+    # 0 (fully masked batch), 1, tile edges, beyond Nk (clamped) and negative (clamped to 0)
+    kl = [0, 1, 63, 64, 65, 500, -3, 129]
+    inp = random_case(8, 2, 130, 300, d, BF16, seed=d, device=DEV, key_lens=kl)
+    forward_and_check(inp, causal, what="bf16 key_lens")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("sigma", [3.0, 12.0])
+def test_bf16_high_dynamic_range(d, sigma):
+    inp = random_case(2, 4, 256, 640, d, BF16, seed=17, device=DEV, q_sigma=sigma, key_lens=[640, 333])
+    forward_and_check(inp, False, what=f"bf16 q~N(0,{sigma ** 2:g})")
+    forward_and_check(inp, True, what=f"bf16 q~N(0,{sigma ** 2:g}) causal")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_no_keys_gives_zero_and_neg_inf(dtype):
+    q = torch.randn(2, 3, 40, 64, device=DEV).to(dtype)
+    k = torch.empty(2, 3, 0, 64, device=DEV, dtype=dtype)
+    o = torch.full_like(q, 7.0)
+    lse = torch.zeros(2, 3, 40, device=DEV)
+    say("[gpu] fa_forward Nk=0")
+    fa.fa_forward(q, k, k, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_bf16_deterministic_and_scale():
+    inp = random_case(2, 8, 384, 384, 128, BF16, seed=5, device=DEV)
+    o1, l1 = fa.attention(inp["q"], inp["k"], inp["v"], causal=True)
+    o2, l2 = fa.attention(inp["q"], inp["k"], inp["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    forward_and_check(inp, True, scale=0.37, what="bf16 scale 0.37")
+
+
+# ------------------------------------------------- full-size workloads, sampled
+@pytest.mark.parametrize("name", ["causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128",
+                                  "masked_bf16_b2h8_n4096_d128"])
+def test_workload_full_size_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w, device=DEV)
+    rows = sample_rows(w.B, w.H, w.N, per_head=6, seed=1, bh_limit=16)
+    eo, el, o, lse = forward_and_check(inp, w.causal, what=name, rows=rows)
+    say(f"    sampled {len(rows)} rows: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+    # properties over every row
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    if w.key_lens:
+        kl = inp["key_lens"].tolist()
+        for b in range(w.B):
+            if kl[b] == 0:
+                assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
+            else:
+                assert torch.all(torch.isfinite(lse[b]))
+    else:
+        assert torch.all(torch.isfinite(lse))
+
+
+# ------------------------------------------------------------------ decode
+def _decode_check(inp, S, what):
+    q, k, v, kl = inp["q"], inp["k"], inp["v"], inp["key_lens"]
+    say(f"[gpu] fa_decode_splitkv {what} B={q.shape[0]} H={q.shape[1]} Nk={k.shape[2]} "
+        f"d={q.shape[3]} {q.dtype} splits={S}")
+    o, lse = fa.decode(q, k, v, num_splits=S, key_lens=kl)
+    torch.cuda.synchronize()
+    d = q.shape[3]
+    O_ref, L_ref = oracle.attention(to_host(q), to_host(k), to_host(v),
+                                    scale=float(np.float32(1 / np.sqrt(d))),
+                                    key_lens=None if kl is None else to_host(kl).tolist())
+    return compare(o, lse, O_ref, L_ref, q.dtype, what) + (o, lse)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("S", [1, 2, 16, 37])
+def test_decode_small(dtype, d, S):
+    inp = random_case(3, 2, 1, 1000, d, dtype, seed=S, device=DEV)
+    _decode_check(inp, S, "decode small")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_decode_key_lens_and_empty(dtype):
+    inp = random_case(5, 2, 1, 700, 128, dtype, seed=2, device=DEV, key_lens=[0, 1, 699, 5000, 17])
+    _decode_check(inp, 16, "decode key_lens")
+    inp = random_case(2, 2, 1, 0, 64, dtype, seed=2, device=DEV)
+    _decode_check(inp, 4, "decode Nk=0")
+
+
+def test_decode_matches_forward_and_split_invariance():
+    inp = random_case(4, 4, 1, 3000, 128, F32, seed=8, device=DEV, key_lens=[3000, 2047, 1, 512])
+    q, k, v, kl = inp["q"], inp["k"], inp["v"], inp["key_lens"]
+    o_f, l_f = fa.attention(q, k, v, key_lens=kl)
+    outs = [fa.decode(q, k, v, num_splits=S, key_lens=kl) for S in (1, 2, 4, 16, 64)]
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.allclose(o, o_f, rtol=0, atol=2e-6)
+        assert torch.allclose(l, l_f, rtol=0, atol=5e-6)
+    o1, l1 = fa.decode(q, k, v, num_splits=16, key_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, outs[3][0]) and torch.equal(l1, outs[3][1])
+
+
+def test_decode_workload_full_size_sampled():
+    w = WORKLOADS["decode_bf16_b64h32_nk16384_d128"]
+    inp = make_inputs(w, device=DEV)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    say(f"[gpu] fa_decode_splitkv {w.name}")
+    o, lse = fa.decode(q, k, v, num_splits=w.num_splits)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any() and torch.all(torch.isfinite(lse))
+    rng = np.random.default_rng(4)
+    pairs = [(0, 0), (w.B - 1, w.H - 1)] + [tuple(rng.integers(0, [w.B, w.H])) for _ in range(10)]
+    for b, h in pairs:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        O_ref, L_ref = oracle.attention(to_host(q[sl]), to_host(k[sl]), to_host(v[sl]),
+                                        scale=float(np.float32(w.scale)))
+        compare(o[sl], lse[sl], O_ref, L_ref, q.dtype, f"{w.name} (b={b}, h={h})")
