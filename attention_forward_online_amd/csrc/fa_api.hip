@@ -26,6 +26,7 @@ fa_status from_hip(hipError_t e) {
 constexpr long long kMaxGridX = 0x7fffffffLL;
 constexpr long long kMaxGridYZ = 65535;
 constexpr long long kMaxElems = 1LL << 46;   // far beyond 288 GB of bf16
+constexpr long long kMaxSliceBytes = (1LL << 31) - 256;   // per (b, h) slice
 
 }  // namespace
 
@@ -56,6 +57,9 @@ fa_status fa_forward(const void *Q, const void *K, const void *V, void *O, float
     const long long rows = (long long)B * H * N;
     if (rows == 0) return FA_OK;
     if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    // one (b, h) slice of Q/O or K/V is addressed with 32-bit byte offsets
+    const long long esz = dtype == FA_BF16 ? 2 : 4;
+    if ((long long)(N > Nk ? N : Nk) * d * esz > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
     if (!Q || !O || !LSE) return FA_ERR_INVALID_ARG;
     if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE)) return FA_ERR_INVALID_ARG;
@@ -88,6 +92,7 @@ fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O
     if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA_OK;
     if ((long long)B * H * (long long)Nk * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if ((long long)Nk * d * (dtype == FA_BF16 ? 2 : 4) > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
     if (B > kMaxGridYZ || H > kMaxGridYZ || (long long)B * H > kMaxGridX) return FA_ERR_INVALID_ARG;
     if (!Q || !O || !LSE || !workspace) return FA_ERR_INVALID_ARG;
     if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;

@@ -36,6 +36,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Raw buffer resource over [base, base + bytes): a load at a byte offset
+// >= bytes returns zeros (hardware range check), so ragged tiles need no
+// branches.  0x00020000 is the gfx9-family descriptor word 3 (32-bit data).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the LDS address of 4 consecutive 16-bit elements (a row
+// chunk); lane L receives element L % 4 of the chunks of lanes L/4 + 4t,
+// t = 0..3, as its element t.  A 4 x 16 block whose row r, column chunk q is
+// read by lane 4r + q therefore arrives transposed: lane 4q + u holds column
+// 4q + u of rows 0..3.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ u32x2_t lds_read_tr16(const __attribute__((address_space(3))) uint16_t *p) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p));
+}
+
+// Wait until every vector-memory load of this wave has returned
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Value of lane (lane ^ mask) for masks < 64.
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);

@@ -13,7 +13,8 @@
  * Conventions shared by every entry point
  *   Memory     All tensor pointers are DEVICE pointers, row-major, contiguous:
  *              Q, O [B, H, N, d]; K, V [B, H, Nk, d]; LSE [B, H, N] (fp32).
- *              Q, K, V and O must be 16-byte aligned.
+ *              Q, K, V and O must be 16-byte aligned, and one (b, h) slice of
+ *              Q/O or K/V must stay below 2 GiB (FA_ERR_INVALID_ARG otherwise).
  *   Ownership  The caller allocates and owns every buffer; the library
  *              allocates nothing and keeps no pointer after a call returns.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls

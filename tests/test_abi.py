@@ -71,6 +71,9 @@ def test_forward_rejects_bad_arguments(lib):
     assert fwd(lib, Q=P + 2) == bad and fwd(lib, O=P + 8) == bad and fwd(lib, K=P + 4) == bad
     assert fwd(lib, LSE=P + 2) == bad
     assert fwd(lib, key_lens=P + 1) == bad
+    # one (b, h) slice of 2 GiB or more
+    assert fwd(lib, N=1 << 24, Nk=4, d=64) == bad
+    assert fwd(lib, N=4, Nk=1 << 24, d=64, dtype=fa.FA_F32) == bad
     # grid beyond the hardware limit
     assert fwd(lib, B=65536, H=65536, N=128, d=64) == bad
 
@@ -117,6 +120,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, Nk=-1) == bad and dec(lib, d=0) == bad
     assert dec(lib, scale=float("nan")) == bad
     assert dec(lib, B=70000, ws_bytes=1 << 40) == bad
+    assert dec(lib, B=1, H=1, Nk=1 << 23, ws_bytes=1 << 20) == bad
     assert dec(lib, d=96) == uns and dec(lib, d=256) == uns
     assert dec(lib, S=257, ws_bytes=1 << 30) == uns
     assert dec(lib, scale=0.0) == uns

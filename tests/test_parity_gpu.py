@@ -80,6 +80,25 @@ def test_bf16_high_dynamic_range(d, sigma):
     forward_and_check(inp, True, what=f"bf16 q~N(0,{sigma ** 2:g}) causal")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("slope", [0.02, 0.3, -0.3, 3.0])
+def test_bf16_score_ramps(d, slope):
+    # scores that rise (or fall) steadily along the keys: the running max moves
+    # by less than, or by much more than, the lazy-rescale threshold per tile;
+    # rows of several batches see different key lengths, one of them none
+    B, H, N, Nk = 3, 2, 200, 700
+    g = torch.Generator().manual_seed(11)
+    q = torch.zeros(B, H, N, d)
+    q[..., 0] = 1.0 + 0.1 * torch.rand(B, H, N, generator=g)
+    k = 0.05 * torch.randn(B, H, Nk, d, generator=g)
+    k[..., 0] += slope * torch.arange(Nk, dtype=torch.float32)
+    v = torch.randn(B, H, Nk, d, generator=g)
+    inp = {"q": q.to(BF16).to(DEV), "k": k.to(BF16).to(DEV), "v": v.to(BF16).to(DEV),
+           "key_lens": torch.tensor([700, 0, 333], dtype=torch.int32, device=DEV)}
+    forward_and_check(inp, False, scale=1.0 / 8, what=f"ramp slope {slope}")
+    forward_and_check(inp, True, scale=1.0 / 8, what=f"ramp slope {slope} causal")
+
+
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_no_keys_gives_zero_and_neg_inf(dtype):
     q = torch.randn(2, 3, 40, 64, device=DEV).to(dtype)
