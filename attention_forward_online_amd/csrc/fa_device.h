@@ -64,6 +64,14 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const __attribute__((address_sp
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// max(v, value of lane ^ 32) on the VALU (v_permlane32_swap exchanges the
+// two 32-lane halves), without going through the LDS queue.
+__device__ __forceinline__ float max_xor32(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 // Value of lane (lane ^ mask) for masks < 64.
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);

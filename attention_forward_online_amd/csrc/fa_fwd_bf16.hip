@@ -1,7 +1,7 @@
 // fa_fwd_bf16.hip -- bf16 prefill attention forward on gfx950 matrix cores.
 //
 // Structure ('Online Softmax & FlashAttention' (interview lesson), Step 3):
-// one workgroup owns one block of Br = 128 query rows for the whole loop
+// one workgroup owns a block of Br = 128 query rows for the whole loop
 // (independent of every other block) and streams the K/V tiles of its head
 // through LDS.  For each tile it applies the tile form of the online-softmax
 // recurrence ('Online Softmax -- the mathematical heart of FlashAttention',
@@ -16,32 +16,36 @@
 // computed against a reference of 0 (the guard of that page's Step 1), l stays
 // 0 and the epilogue writes O = 0, LSE = -inf.
 //
-// gfx950 mapping (4 waves, 32 query rows per wave):
+// gfx950 mapping (4 waves, 32 query rows per wave, 64-key tiles):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the Q fragment is the B
 //     operand and stays in VGPRs for the whole loop; K rows come from LDS.
 //     In the 32x32 accumulator each lane holds one query column, so a row
-//     max/sum is an in-lane reduction plus one exchange with lane ^ 32.
+//     max/sum is an in-lane reduction plus one exchange with lane ^ 32
+//     (v_permlane32_swap, no LDS traffic).
 //   * The rows of each 32-key block are read in the order perm32 (bits 2 and
 //     3 of the row index swapped).  Then accumulator registers 8h..8h+7 of
 //     lane half g are keys 16h + 8g + 0..7: converted to bf16 they are the B
-//     operand of O^T = V^T P^T without any data movement, and the matching
-//     A operand is one 16-byte read of V^T from LDS.
+//     operand of O^T = V^T P^T without any data movement.
 //   * K and V tiles are stored row-major in LDS alike; the V^T operand comes
 //     from the gfx950 transpose read (ds_read_b64_tr_b16), two per MFMA.
 //   * Scores stay fp32; exp runs as 2^(s*scale*log2 e - m'), one FMA plus
 //     v_exp_f32 per score; P is rounded to bf16 (RNE) only as the MFMA operand
 //     while the row sum uses the fp32 values.
-//   * Two LDS stages: the next tile's global loads are in flight while the
-//     current tile is computed; one barrier per tile.
+//   * Lazy rescale: the reference max moves only when a tile's max exceeds it
+//     by more than 2^8 (FA-4's thresholded rescale); o and l always share the
+//     reference, so the result is unchanged while most tiles skip the
+//     rescale of the accumulators.
 //   * Work units: a causal workgroup takes query blocks n-1-u and u one after
 //     the other, so every workgroup does the same number of key tiles; all
 //     units of a head run on one XCD (the dispatcher deals workgroup ids to
 //     the 8 XCDs round-robin), so K/V re-reads of a head hit one L2, and
 //     consecutive heads go to different XCDs.
-//   * Lazy rescale: the reference max moves only when a tile's max exceeds it
-//     by more than 2^8 (FA-4's thresholded rescale); o and l always share the
-//     reference, so the result is unchanged while most tiles skip the
-//     rescale of the accumulators.
+//   * Two LDS stages, one barrier per tile: tile t is computed from one stage
+//     while the other receives tile t+1 from registers; the global loads of
+//     tile t+2 are in flight meanwhile.  Tiles are processed in order, with
+//     the two waves of each SIMD (two workgroups per CU) overlapping one
+//     wave's softmax with the other's MFMAs.  (Software-pipelining the next
+//     tile's QK^T into the softmax within a wave measured slower on gfx950.)
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -72,15 +76,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int n_units,
     int xcd_interleave, float c) {
+    constexpr int NST = 2;                      // LDS stages
     constexpr int KS = D + kPad;                // K and V row stride in LDS (elements)
+    constexpr int TILE = kBc * KS;              // elements per stage of K (or V)
     constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
     constexpr int CB = D / 32;                  // 32-column blocks of O^T
     constexpr int KCH = kBc * D / 8;            // 16-byte chunks per K (or V) tile
     constexpr int KL = KCH / kThreads;          // ... per thread
     static_assert(KCH % kThreads == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBc * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBc * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[NST * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[NST * TILE];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, g = lane >> 5;
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int vrow = (li & 15) >> 2;
     const int vcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
     const __attribute__((address_space(3))) uint16_t *vs_lds =
-        (const __attribute__((address_space(3))) uint16_t *)&Vs[0][0];
+        (const __attribute__((address_space(3))) uint16_t *)&Vs[0];
 
     // workgroup -> (head, unit).  With B*H divisible by 8, head bh lives on
     // XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs round-robin):
@@ -149,121 +155,141 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         float ms = neg_inf();
         float l = 0.f;          // this lane's half of the running denominator
 
-        u32x4_t kreg[KL];
-        u32x4_t vreg[KL];
-        auto gload = [&](int t) {
+        // Register stage for the global -> LDS copy.  Loads past the last tile
+        // fall outside the buffer range and return zeros without touching
+        // memory, so they are issued unconditionally (straight-line code keeps
+        // the vmcnt waits partial).
+        u32x4_t kr[KL], vr[KL];
+        auto gload = [&](int t, u32x4_t (&kr)[KL], u32x4_t (&vr)[KL]) {
             const int j0 = t * kBc;
 #pragma unroll
             for (int p = 0; p < KL; ++p) {
                 const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-                kreg[p] = buffer_load16(ksrc, (uint32_t)((j0 + row) * D + 8 * col8) * 2);
-            }
-#pragma unroll
-            for (int p = 0; p < KL; ++p) {
-                const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-                vreg[p] = buffer_load16(vsrc, (uint32_t)((j0 + row) * D + 8 * col8) * 2);
+                const uint32_t off_b = (uint32_t)((j0 + row) * D + 8 * col8) * 2;
+                kr[p] = buffer_load16(ksrc, off_b);
+                vr[p] = buffer_load16(vsrc, off_b);
             }
         };
-        auto lstore = [&](int buf) {
+        auto lstore = [&](int stage, const u32x4_t (&kr)[KL], const u32x4_t (&vr)[KL]) {
 #pragma unroll
             for (int p = 0; p < KL; ++p) {
                 const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-                *(u32x4_t *)&Ks[buf][row * KS + 8 * col8] = kreg[p];
-                *(u32x4_t *)&Vs[buf][row * KS + 8 * col8] = vreg[p];
+                *(u32x4_t *)&Ks[stage * TILE + row * KS + 8 * col8] = kr[p];
+                *(u32x4_t *)&Vs[stage * TILE + row * KS + 8 * col8] = vr[p];
             }
+        };
+        auto active = [&](int t) {   // wave-uniform; a prefix of the tiles
+            return wq_first <= wq_last && (!CAUSAL || t * kBc <= wq_last + off);
+        };
+        // S^T of one 64-key tile (two 32-key blocks) x this wave's 32 queries,
+        // operands read from LDS as the MFMAs need them
+        auto qk_lds = [&](int stage, f32x16_t (&s)[2]) {
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const uint16_t *kp = &Ks[stage * TILE + (32 * jb + krow) * KS + 8 * g];
+                s[jb] = mfma32(*(const u32x4_t *)kp, qf[0], f32x16_t{});
+#pragma unroll
+                for (int kk = 1; kk < KK; ++kk)
+                    s[jb] = mfma32(*(const u32x4_t *)(kp + 16 * kk), qf[kk], s[jb]);
+            }
+        };
+        // V^T operand (A of the P.V MFMA) for keys 32jb + 16h + 8g + 0..7 and
+        // V column 32cb + perm32(li) of the tile in `stage`
+        auto v_operand = [&](int stage, int cb, int jb, int h) {
+            const auto *p0 =
+                vs_lds + stage * TILE + (8 * g + vrow + 32 * jb + 16 * h) * KS + vcol + 32 * cb;
+            const u32x2_t lo = lds_read_tr16(p0);
+            const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
+            return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        };
+        // masking, row max and the (rare) move of the reference; returns the
+        // reference the probabilities of this tile use
+        auto softmax_prep = [&](int t, f32x16_t (&sc)[2]) {
+            const int j0 = t * kBc;
+            const bool need_mask =
+                (j0 + kBc > kv_lim) || (CAUSAL && j0 + kBc - 1 > wq_first + off);
+            if (need_mask) {
+                // register v of block jb holds key j0 + 32jb + 16(v/8) + 8g + v%8;
+                // keys at or past this lane's limit are invisible
+                const int vis_end = CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim;
+                const int lim = vis_end - j0 - 8 * g;
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) sc[jb][v] = neg_inf();
+            }
+            // tile row max: four independent chains over the 32 in-lane keys,
+            // the other 32 keys in lane ^ 32
+            float m4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x16_t &s = sc[i >> 1];
+                const int v0 = 8 * (i & 1);
+                m4[i] = fmaxf(fmaxf(fmaxf(s[v0], s[v0 + 1]), s[v0 + 2]),
+                              fmaxf(fmaxf(s[v0 + 3], s[v0 + 4]),
+                                    fmaxf(fmaxf(s[v0 + 5], s[v0 + 6]), s[v0 + 7])));
+            }
+            const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+            // move the reference only when this row's max got too far ahead
+            const bool move = mx > ms + kLazyTau;   // false for a fully masked tile
+            if (__any(move)) {
+                // lanes that keep their reference use alpha = 1 (never
+                // exp2(ms - ms), which is NaN while ms is still -inf)
+                const float alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
+                l *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
+                ms = move ? mx : ms;
+            }
+            return ms == neg_inf() ? 0.f : ms;   // -inf guard: all P = 0 then
+        };
+        // P = 2^(s c - ref) for this lane's 32 scores: bf16 pairs for the MFMA,
+        // fp32 values into the row sum (four partial sums)
+        auto probabilities = [&](const f32x16_t (&sc)[2], float ms_ref, uint32_t (&pk)[2][8]) {
+            float r4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const float p0 = exp2_hw(fmaf(sc[jb][v], c, -ms_ref));
+                    const float p1 = exp2_hw(fmaf(sc[jb][v + 1], c, -ms_ref));
+                    r4[(v >> 1) & 3] += p0 + p1;
+                    pk[jb][v >> 1] = pack_bf16x2(p0, p1);
+                }
+            return (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        };
+        auto p_operand = [&](const uint32_t (&pk)[2][8], int jb, int h) {
+            return u32x4_t{pk[jb][4 * h], pk[jb][4 * h + 1], pk[jb][4 * h + 2], pk[jb][4 * h + 3]};
         };
 
-        if (ntiles > 0) {
-            gload(0);
-            lstore(0);
-        }
+        // tiles in order from two LDS stages; the loads of tile t+1 are in
+        // flight while tile t is computed
+        gload(0, kr, vr);
+        lstore(0, kr, vr);
+        gload(1, kr, vr);
         __syncthreads();
-
         for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            const int j0 = t * kBc;
-            if (t + 1 < ntiles) gload(t + 1);
-
-            const bool active = wq_first <= wq_last && (!CAUSAL || j0 <= wq_last + off);
-            if (active) {
-                // S^T for keys j0 .. j0+63 (two 32-key blocks) x this wave's 32 queries
-                f32x16_t s[2];
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) s[jb][v] = 0.f;
-                    const uint16_t *kp = &Ks[buf][(32 * jb + krow) * KS + 8 * g];
-#pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        s[jb] = mfma32(*(const u32x4_t *)(kp + 16 * kk), qf[kk], s[jb]);
-                }
-                // mask: key length, ragged end, causal diagonal
-                const bool need_mask =
-                    (j0 + kBc > kv_lim) || (CAUSAL && j0 + kBc - 1 > wq_first + off);
-                if (need_mask) {
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int key = j0 + 32 * jb + 16 * (v >> 3) + 8 * g + (v & 7);
-                            const bool ok = key < kv_lim && (!CAUSAL || key <= qrow + off);
-                            if (!ok) s[jb][v] = neg_inf();
-                        }
-                }
-                // tile row max: 32 keys in-lane, the other 32 in lane ^ 32
-                float mx = s[0][0];
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[jb][v]);
-                mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * c;
-                // move the reference only when this row's max got too far ahead
-                const bool move = mx > ms + kLazyTau;   // false for a fully masked tile
-                if (__any(move)) {
-                    // lanes that keep their reference use alpha = 1 (never
-                    // exp2(ms - ms), which is NaN while ms is still -inf)
-                    const float alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
-                    l *= alpha;
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
-                    ms = move ? mx : ms;
-                }
-                const float ms_ref = ms == neg_inf() ? 0.f : ms;   // -inf guard: all P = 0 then
-
+            const int cur = t & 1;
+            if (active(t)) {
+                f32x16_t sc[2];
+                qk_lds(cur, sc);
+                const float ms_ref = softmax_prep(t, sc);
                 uint32_t pk[2][8];
-                float rs = 0.f;
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int v = 0; v < 16; v += 2) {
-                        const float p0 = exp2_hw(fmaf(s[jb][v], c, -ms_ref));
-                        const float p1 = exp2_hw(fmaf(s[jb][v + 1], c, -ms_ref));
-                        rs += p0 + p1;
-                        pk[jb][v >> 1] = pack_bf16x2(p0, p1);
-                    }
-                l += rs;
-                // O^T += V^T P^T
-                const __attribute__((address_space(3))) uint16_t *vp =
-                    vs_lds + buf * (kBc * KS) + (8 * g + vrow) * KS + vcol;
+                l += probabilities(sc, ms_ref, pk);
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            // keys 32jb + 16h + 8g + 0..7 of V column 32cb + perm32(li)
-                            const auto *p0 = vp + (32 * jb + 16 * h) * KS + 32 * cb;
-                            const u32x2_t lo = lds_read_tr16(p0);
-                            const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
-                            const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-                            const u32x4_t bop = {pk[jb][4 * h], pk[jb][4 * h + 1],
-                                                 pk[jb][4 * h + 2], pk[jb][4 * h + 3]};
-                            acc[cb] = mfma32(aop, bop, acc[cb]);
-                        }
+                        for (int h = 0; h < 2; ++h)
+                            acc[cb] = mfma32(v_operand(cur, cb, jb, h), p_operand(pk, jb, h),
+                                             acc[cb]);
             }
-            if (t + 1 < ntiles) lstore(buf ^ 1);
+            lstore(cur ^ 1, kr, vr);    // tile t+1
+            gload(t + 2, kr, vr);
             __syncthreads();
         }
 
@@ -286,6 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             if (g == 0)
                 LSE[(size_t)bh * N + qrow] = lt > 0.f ? (ms + log2_hw(lt)) * kLn2 : neg_inf();
         }
+        __syncthreads();   // the next block's prologue rewrites the LDS stages
     }
 }
 
