@@ -29,6 +29,7 @@ METRIC = "fused attention fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB
 HEADLINE = "causal_bf16_b4h16_n2048_d64"
 DECODE = "decode_bf16_b64h32_nk16384_d128"
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 512 * 1024 * 1024   # plain copy for counter calibration
 
 
 def prefill_flops(w, key_lens=None):
@@ -45,27 +46,22 @@ def decode_bytes(w):
     return (2 * w.B * w.H * w.Nk * w.d + 2 * w.B * w.H * w.d) * el + w.B * w.H * 4
 
 
-def time_launches(fn, steps, warmup):
-    """Per-launch HIP event times (ms) on torch's current stream, which is the
-    stream the library launches on; also the total over the timed region."""
+def time_region(fn, steps, warmup):
+    """Milliseconds per call: HIP events on torch's current stream (the stream
+    the library launches on) bracket `steps` back-to-back calls, after
+    `warmup` untimed calls and a device synchronisation on both sides."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
-    for a, b in ev:
-        a.record()
+    for _ in range(steps):
         fn()
-        b.record()
     t1.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return per, t0.elapsed_time(t1)
+    return t0.elapsed_time(t1) / steps
 
 
 def kernel_source_hash():
@@ -100,6 +96,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true",
                     help="time only the headline prefill (used under the profiler)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the split-KV decode (used under the profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE "
+                         "counters scale the kernel's counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -119,17 +120,27 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda"
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---------------------------------------------------------------- headline
     w = WORKLOADS[HEADLINE]
     inp = make_inputs(w, device=dev)
     q, k, v = inp["q"], inp["k"], inp["v"]
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
-    per, total = time_launches(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
-                               args.steps, args.warmup)
+    # one fa_forward call launches exactly one kernel, so the time per step is
+    # that kernel's average launch duration (plus any gap between launches)
+    ms_step = time_region(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
+                          args.steps if not args.only_decode else 1,
+                          args.warmup if not args.only_decode else 0)
     flops = prefill_flops(w)
-    ms_step = total / args.steps
-    avg_launch = float(np.mean(per))
+    avg_launch = ms_step
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (avg_launch * 1e-3) / 1e12
     traffic = measured_traffic("fwd_bf16_kernel<64,true>/" + HEADLINE)
@@ -156,6 +167,8 @@ def main():
     }
     head_out = (o, lse)
 
+    if args.only_decode:
+        out = {"metric": METRIC}
     if not args.only_headline:
         # ------------------------------------------------------------ decode
         wd = WORKLOADS[DECODE]
@@ -165,13 +178,12 @@ def main():
         nb = fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits)
         ws = torch.empty(nb // 4, device=dev, dtype=torch.float32)
         dsteps = max(5, args.steps // 5)
-        per_d, tot_d = time_launches(
+        ms_d = time_region(
             lambda: fa.fa_decode_splitkv(di["q"], di["k"], di["v"], od, ld, wd.num_splits, ws),
             dsteps, max(2, args.warmup // 2))
         nbytes = decode_bytes(wd)
-        ms_d = tot_d / dsteps
         gbs = nbytes / (ms_d * 1e-3) / 1e9
-        gbs_launch = nbytes / (float(np.mean(per_d)) * 1e-3) / 1e9
+        gbs_launch = gbs   # split + combine, the whole call
         out["decode"] = {
             "workload": wd.describe(), "name": DECODE, "value": round(gbs, 1), "unit": "GB/s",
             "ms_per_call": round(ms_d, 4), "bytes_per_call": nbytes,
@@ -184,6 +196,7 @@ def main():
         del di, od, ld, ws
         torch.cuda.empty_cache()
 
+    if not args.only_headline and not args.only_decode:
         # ------------------------------------------------- other prefill shapes
         others = {}
         for name in ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",
@@ -194,10 +207,9 @@ def main():
             ol = torch.empty(wo.B, wo.H, wo.N, device=dev, dtype=torch.float32)
             kl = oi["key_lens"]
             st = max(5, args.steps // 5)
-            per_o, tot_o = time_launches(
+            ms_o = time_region(
                 lambda: fa.fa_forward(oi["q"], oi["k"], oi["v"], oo, ol, causal=wo.causal,
                                       key_lens=kl), st, 3)
-            ms_o = float(np.mean(per_o))
             nominal = prefill_flops(wo)
             rec = {"workload": wo.describe(), "ms_per_call": round(ms_o, 5),
                    "tflops_nominal": round(nominal / (ms_o * 1e-3) / 1e12, 2)}
@@ -215,7 +227,7 @@ def main():
         out["workloads"] = others
 
     # ------------------------------------------------------- CPU oracle baseline
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.only_decode:
         import oracle
         nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
         qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
