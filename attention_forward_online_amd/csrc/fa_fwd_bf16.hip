@@ -35,11 +35,15 @@
 //     by more than 2^8 (FA-4's thresholded rescale); o and l always share the
 //     reference, so the result is unchanged while most tiles skip the
 //     rescale of the accumulators.
-//   * Work units: a causal workgroup takes query blocks n-1-u and u one after
-//     the other, so every workgroup does the same number of key tiles; all
-//     units of a head run on one XCD (the dispatcher deals workgroup ids to
-//     the 8 XCDs round-robin), so K/V re-reads of a head hit one L2, and
-//     consecutive heads go to different XCDs.
+//   * Work order: one query block per workgroup, causal launches start with
+//     the longest blocks; all blocks of a head run on one XCD (the dispatcher
+//     deals workgroup ids to the 8 XCDs round-robin), so K/V re-reads of a
+//     head hit one L2, and consecutive heads go to different XCDs.  (Pairing
+//     blocks n-1-u and u in one workgroup evens the work but halves the
+//     waves per SIMD; it measured slower.)
+//   * The MFMA sections run at raised wave priority (s_setprio 1), so the
+//     arbiter issues a waiting wave's MFMAs ahead of the other wave's VALU
+//     work and the matrix pipe stays fed.
 //   * Two LDS stages, one barrier per tile: tile t is computed from one stage
 //     while the other receives tile t+1 from registers; the global loads of
 //     tile t+2 are in flight meanwhile.  Tiles are processed in order, with
@@ -70,12 +74,13 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
-    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int n_units,
-    int xcd_interleave, float c) {
+    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
+    float c) {
     constexpr int NST = 2;                      // LDS stages
     constexpr int KS = D + kPad;                // K and V row stride in LDS (elements)
     constexpr int TILE = kBc * KS;              // elements per stage of K (or V)
@@ -99,18 +104,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const __attribute__((address_space(3))) uint16_t *vs_lds =
         (const __attribute__((address_space(3))) uint16_t *)&Vs[0];
 
-    // workgroup -> (head, unit).  With B*H divisible by 8, head bh lives on
+    // workgroup -> (head, query block).  With B*H divisible by 8, head bh lives on
     // XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs round-robin):
-    // all units of a head share one L2 and neighbouring heads spread over XCDs.
-    const int BH = gridDim.x / n_units;
+    // all blocks of a head share one L2 and neighbouring heads spread over XCDs.
+    const int BH = gridDim.x / n_qtiles;
     const int bid = blockIdx.x;
-    int unit, bh;
+    int rank, bh;                   // rank: position of the block in launch order
     if (xcd_interleave) {
         const int hpx = BH >> 3, slot = bid >> 3;
-        unit = slot / hpx;
+        rank = slot / hpx;
         bh = (slot % hpx) * 8 + (bid & 7);
     } else {
-        unit = bid / BH;
+        rank = bid / BH;
         bh = bid % BH;
     }
     const int b = bh / H;
@@ -120,11 +125,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const size_t kv_base = (size_t)bh * Nk * D;
     const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);   // rows >= N read as 0
 
-    // A causal unit is the pair of query blocks (n-1-u, u): every unit then has
-    // the same number of key tiles.  A non-causal unit is one block.
-    const int nblk = (CAUSAL && n_qtiles - 1 - unit != unit) ? 2 : 1;
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int qtile = CAUSAL ? (blk == 0 ? n_qtiles - 1 - unit : unit) : unit;
+    // One query block per workgroup; causal launches hand out the longest
+    // blocks (the last ones) first.
+    {
+        const int qtile = CAUSAL ? n_qtiles - 1 - rank : rank;
         const int q0 = qtile * kBr;
         int kv_end = kv_lim;
         if (CAUSAL) kv_end = min(kv_end, min(q0 + kBr, N) - 1 + off + 1);
@@ -275,10 +279,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int cur = t & 1;
             if (active(t)) {
                 f32x16_t sc[2];
+                __builtin_amdgcn_s_setprio(1);
                 qk_lds(cur, sc);
+                __builtin_amdgcn_s_setprio(0);
                 const float ms_ref = softmax_prep(t, sc);
                 uint32_t pk[2][8];
                 l += probabilities(sc, ms_ref, pk);
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -287,6 +294,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                         for (int h = 0; h < 2; ++h)
                             acc[cb] = mfma32(v_operand(cur, cb, jb, h), p_operand(pk, jb, h),
                                              acc[cb]);
+                __builtin_amdgcn_s_setprio(0);
             }
             lstore(cur ^ 1, kr, vr);    // tile t+1
             gload(t + 2, kr, vr);
@@ -312,21 +320,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             if (g == 0)
                 LSE[(size_t)bh * N + qrow] = lt > 0.f ? (ms + log2_hw(lt)) * kLn2 : neg_inf();
         }
-        __syncthreads();   // the next block's prologue rewrites the LDS stages
     }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
-    const int n_units = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
     const long long BH = (long long)a.B * a.H;
-    const long long nblocks = BH * n_units;
+    const long long nblocks = BH * n_qtiles;
     const int xcd_interleave = (BH % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
                        stream, (const uint16_t *)a.Q, (const uint16_t *)a.K,
                        (const uint16_t *)a.V, (uint16_t *)a.O, a.LSE, a.key_lens, a.H, a.N,
-                       a.Nk, n_qtiles, n_units, xcd_interleave, a.scale * kLog2e);
+                       a.Nk, n_qtiles, xcd_interleave, a.scale * kLog2e);
     return hipGetLastError();
 }
 
