@@ -10,7 +10,10 @@
 // with the reference m replaced by 0 when both sides are -inf.
 //
 // The split kernel is bound by the K/V stream from HBM, so it uses no matrix
-// instruction: each lane owns 16 bytes of a key row (8 bf16 or 4 fp32), a key
+// instruction.  K and V are read once, with nontemporal loads (they would only
+// evict reusable lines from the caches), 16 rows of each in flight per lane
+// (measured 6.83 TB/s, against 7.0 TB/s for a pure streaming read on the same
+// 16 GiB).  Each lane owns 16 bytes of a key row (8 bf16 or 4 fp32), a key
 // row is spread over LPR consecutive lanes whose partial dot products are
 // summed by lane exchanges, and one wave-wide 16-byte load covers 64/LPR key
 // rows.  Each group of LPR lanes keeps its own running (m, l, o) over the rows
@@ -28,7 +31,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 8;    // key-row loads per lane in flight per iteration
+constexpr int kUnroll = 16;   // key-row loads of K (and of V) per lane in flight per iteration
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {   // bf16
@@ -112,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         for (int u = 0; u < kUnroll; ++u) {
             const int row = base + u * RPW + rg;
             const bool in = row < k_end;
-            kr[u] = in ? *(const u32x4_t *)(kp + (size_t)row * D) : u32x4_t{0, 0, 0, 0};
-            vr[u] = in ? *(const u32x4_t *)(vp + (size_t)row * D) : u32x4_t{0, 0, 0, 0};
+            kr[u] = in ? __builtin_nontemporal_load((const u32x4_t *)(kp + (size_t)row * D)) : u32x4_t{0, 0, 0, 0};
+            vr[u] = in ? __builtin_nontemporal_load((const u32x4_t *)(vp + (size_t)row * D)) : u32x4_t{0, 0, 0, 0};
         }
         float s[kUnroll];
 #pragma unroll
