@@ -48,6 +48,9 @@ def load(path: str = _LIB_PATH, rebuild_if_missing: bool = True):
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
         dp, dp, ctypes.c_int]
     lib.oracle_attention_f64.restype = ctypes.c_int
+    lib.oracle_softmax_rows_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_long,
+                                            ctypes.c_long, ctypes.c_void_p, dp]
+    lib.oracle_softmax_rows_f64.restype = ctypes.c_int
     return lib
 
 
@@ -146,3 +149,24 @@ def attention(q, k, v, scale=None, causal=False, key_lens=None, rows=None, nthre
     if rows is None:
         return O.reshape(B, H, N, d), LSE.reshape(B, H, N)
     return O, LSE
+
+
+def softmax_rows(x, want_y=True, lib=None):
+    """Row-wise three-pass softmax of a [rows, cols] matrix (-inf entries masked).
+
+    Returns (Y or None, LSE) as float64 arrays; LSE = -inf for a fully masked row.
+    """
+    lib = lib or _get()
+    xa, dt = _host_array(x)
+    if xa.ndim != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = xa.shape
+    Y = np.zeros((rows, cols), dtype=np.float64) if want_y else None
+    LSE = np.zeros((rows,), dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_softmax_rows_f64(xa.ctypes.data if xa.size else None, dt, rows, cols,
+                                     Y.ctypes.data if Y is not None else None,
+                                     LSE.ctypes.data_as(dp))
+    if rc != 0:
+        raise RuntimeError(f"oracle_softmax_rows_f64 returned {rc}")
+    return Y, LSE

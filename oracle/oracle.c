@@ -35,6 +35,11 @@
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -pthread oracle.c -lm
  * (no fast-math: -inf must stay IEEE -inf).
  *
+ * The row-wise softmax (oracle_softmax_rows_f64) is the same three-pass
+ * definition applied to every row of a matrix; it checks the streaming
+ * softmax / log-sum-exp kernel ('Online Softmax' research-hub page, "Why it
+ * matters": the recurrence also streams rows too wide for on-chip memory).
+ *
  * Parity pins (tests/test_oracle.py): the worked softmax examples printed on
  * the pages, the chunk-merge invariant of 'Online Softmax & FlashAttention'
  * Step 1, the tiled V1 shapes of its Step 2, closed forms, invariants and a
@@ -91,6 +96,35 @@ int oracle_softmax_f64(const double *x, long n, double *y, double *m_out, double
             y[j] = exp(x[j] - m) / l;
     *m_out = m;
     *l_out = l;
+    return 0;
+}
+
+/*
+ * Row-wise softmax of a [rows, cols] matrix in fp64: every row goes through
+ * the three-pass definition above (-inf entries masked).  X has element type
+ * `dtype` (0 = fp64, 1 = fp32, 2 = bf16 bits).  Y: fp64 [rows, cols] or NULL;
+ * LSE: fp64 [rows], m + ln l, -inf for a fully masked row.  Returns 0, -1 for
+ * invalid arguments, -2 when memory runs out.
+ */
+int oracle_softmax_rows_f64(const void *X, int dtype, long rows, long cols, double *Y,
+                            double *LSE)
+{
+    double *x, m, l;
+    long r, j;
+    if (rows < 0 || cols < 0 || dtype < ORACLE_F64 || dtype > ORACLE_BF16 || !LSE)
+        return -1;
+    if (rows > 0 && cols > 0 && !X)
+        return -1;
+    x = (double *)malloc(sizeof(double) * (size_t)(cols > 0 ? cols : 1));
+    if (!x)
+        return -2;
+    for (r = 0; r < rows; ++r) {
+        for (j = 0; j < cols; ++j)
+            x[j] = widen(X, dtype, (size_t)r * cols + j);
+        oracle_softmax_f64(x, cols, Y ? Y + (size_t)r * cols : NULL, &m, &l);
+        LSE[r] = l > 0.0 ? m + log(l) : -INFINITY;
+    }
+    free(x);
     return 0;
 }
 

@@ -323,8 +323,40 @@ def check_rows_and_threads(lib):
     assert np.array_equal(Ob[0], O0[0]) and np.array_equal(Ob[1], O1[0])
 
 
+def check_softmax_rows(lib):
+    # every row equals the single-vector softmax; LSE is the library logsumexp
+    X, widths, g = _chunk_matrix()
+    Y, L = oracle.softmax_rows(X, lib=lib)
+    for r in range(X.shape[0]):
+        y, m, l = oracle.softmax(X[r], lib=lib)
+        assert np.array_equal(Y[r], y)
+        ref = scipy.special.logsumexp(X[r]) if np.isfinite(X[r]).any() else -np.inf
+        assert (L[r] == -np.inf and ref == -np.inf) or abs(L[r] - ref) <= TIGHT
+    fin = np.isfinite(X).any(axis=1)
+    assert np.allclose(Y[fin], scipy.special.softmax(np.where(np.isfinite(X), X, -np.inf)[fin], axis=1),
+                       rtol=0, atol=TIGHT)
+    # worked example through the rows entry, fp32 and bf16 storage widen exactly
+    Yw, Lw = oracle.softmax_rows(np.array([[1.0, 3.0, 2.0], [1.0, 3.0, 2.0]], dtype=np.float32), lib=lib)
+    gw = _golden("softmax_worked_example.txt")
+    tol = 0.5 * 10 ** (-int(gw["decimals"][0][0])) + 1e-12
+    assert np.all(np.abs(Yw - _floats(gw["y"][0])) <= tol)
+    assert abs(math.exp(Lw[0] - 3.0) - float(gw["sum"][0][0])) <= tol
+    xb = torch.tensor([[0.5, -2.0, 7.25, 3.0]]).to(torch.bfloat16)
+    Yb, Lb = oracle.softmax_rows(xb, lib=lib)
+    assert abs(Lb[0] - scipy.special.logsumexp(xb.double().numpy()[0])) <= TIGHT
+    # shift invariance: softmax(x + c) = softmax(x), LSE(x + c) = LSE(x) + c
+    r = _rng(41).standard_normal((3, 50))
+    Y1, L1 = oracle.softmax_rows(r, lib=lib)
+    Y2, L2 = oracle.softmax_rows(r + 7.5, lib=lib)
+    assert np.allclose(Y1, Y2, rtol=0, atol=TIGHT) and np.allclose(L1 + 7.5, L2, rtol=0, atol=1e-11)
+    # empty rows
+    Ye, Le = oracle.softmax_rows(np.zeros((2, 0)), lib=lib)
+    assert Ye.shape == (2, 0) and np.all(Le == -np.inf)
+
+
 ALL_CHECKS = [
     check_worked_example, check_four_element, check_x153, check_chunk_merge,
     check_merge_guard_negative_control, check_tiled_shapes, check_closed_forms,
     check_invariants, check_torch_sdpa, check_bf16_widening, check_rows_and_threads,
+    check_softmax_rows,
 ]

@@ -29,6 +29,8 @@ MUTANTS = {
     "softmax_no_shift": ("y[j] = exp(x[j] - m) / l;", "y[j] = exp(x[j]) / l;"),
     "softmax_min_not_max": ("if (x[j] > m)\n            m = x[j];", "if (x[j] > m && m == -INFINITY)\n            m = x[j];"),
     "masked_row_lse_zero": ("a->LSE[out_row] = -INFINITY;\n        return;", "a->LSE[out_row] = 0.0;\n        return;"),
+    "rows_lse_drops_max": ("LSE[r] = l > 0.0 ? m + log(l) : -INFINITY;", "LSE[r] = l > 0.0 ? log(l) : -INFINITY;"),
+    "rows_wrong_stride": ("x[j] = widen(X, dtype, (size_t)r * cols + j);", "x[j] = widen(X, dtype, (size_t)r + j);"),
     "row_index_swapped": ("long bh = flat / a->N, i = flat % a->N, b = bh / a->H;",
                           "long bh = flat / a->N, i = flat % a->N, b = bh % a->B;"),
 }
