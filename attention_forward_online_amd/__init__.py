@@ -5,8 +5,10 @@ include/fa.h); this package only marshals torch tensors into that ABI.
 """
 from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_F32,
                  FA_OK, FaError, attention, decode, fa_decode_splitkv, fa_decode_workspace_bytes,
-                 fa_forward, load_library, status_str)
+                 fa_forward, fa_softmax, fa_softmax_workspace_bytes, load_library, softmax,
+                 status_str)
 
 __all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_F32",
            "FA_OK", "FaError", "attention", "decode", "fa_decode_splitkv",
-           "fa_decode_workspace_bytes", "fa_forward", "load_library", "status_str"]
+           "fa_decode_workspace_bytes", "fa_forward", "fa_softmax", "fa_softmax_workspace_bytes",
+           "load_library", "softmax", "status_str"]

@@ -27,6 +27,7 @@ constexpr long long kMaxGridX = 0x7fffffffLL;
 constexpr long long kMaxGridYZ = 65535;
 constexpr long long kMaxElems = 1LL << 46;   // far beyond 288 GB of bf16
 constexpr long long kMaxSliceBytes = (1LL << 31) - 256;   // per (b, h) slice
+constexpr long long kMaxSoftmaxCols = 1LL << 30;         // chunk indices stay 32-bit
 
 }  // namespace
 
@@ -105,6 +106,31 @@ fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O
     fa::DecodeArgs a{Q, K, V, O, LSE, key_lens, B, H, Nk, d, scale, num_splits,
                      static_cast<float *>(workspace)};
     return from_hip(fa::launch_decode(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_softmax_workspace_bytes(int64_t rows, int64_t cols, fa_dtype dtype) {
+    if (rows < 0 || cols < 0 || (dtype != FA_F32 && dtype != FA_BF16)) return 0;
+    if ((long long)rows * (long long)cols > kMaxElems || cols > kMaxSoftmaxCols) return 0;
+    return fa::softmax_workspace_bytes(rows, cols, dtype == FA_BF16);
+}
+
+fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t cols,
+                     fa_dtype dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 0) return FA_ERR_INVALID_ARG;
+    if (rows == 0) return FA_OK;
+    if (cols > kMaxSoftmaxCols || (long long)rows * (long long)cols > kMaxElems)
+        return FA_ERR_INVALID_ARG;
+    if (rows > kMaxGridX) return FA_ERR_INVALID_ARG;
+    if (!LSE || !aligned4(LSE)) return FA_ERR_INVALID_ARG;
+    if (cols > 0 && (!X || !aligned16(X))) return FA_ERR_INVALID_ARG;
+    if (Y && !aligned16(Y)) return FA_ERR_INVALID_ARG;
+    const size_t need = fa::softmax_workspace_bytes(rows, cols, dtype == FA_BF16);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+        return FA_ERR_INVALID_ARG;
+    if (cols == 0) Y = nullptr;   // nothing to write but lse = -inf
+    fa::SoftmaxArgs a{X, Y, LSE, rows, cols, workspace};
+    return from_hip(fa::launch_softmax(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

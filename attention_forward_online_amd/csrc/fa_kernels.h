@@ -29,11 +29,23 @@ struct DecodeArgs {
     float *workspace;           // B*H*num_splits*(d+2) floats
 };
 
+struct SoftmaxArgs {
+    const void *X;
+    void *Y;                    // nullptr: log-sum-exp only
+    float *LSE;
+    long long rows, cols;
+    void *workspace;            // softmax_workspace_bytes(rows, cols, ...) bytes
+};
+
 // bf16 prefill, d in {64, 128}: MFMA 32x32x16 bf16 tiles.
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 // fp32 prefill, 1 <= d <= 256: fp32 FMA tiles.
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 // split-KV decode, d in {64, 128}; is_bf16 selects the element type.
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
+
+// Row softmax / log-sum-exp of a [rows, cols] fp32 or bf16 matrix.
+size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16);
+hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream);
 
 }  // namespace fa

@@ -20,8 +20,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_BF16 = 0, 1
 
 #: every symbol include/fa.h declares
-EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_status_str",
-           "fa_last_hip_error")
+EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+           "fa_softmax_workspace_bytes", "fa_softmax", "fa_status_str", "fa_last_hip_error")
 
 _lib = None
 
@@ -49,6 +49,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, i, vp, sz, i, vp]
     lib.fa_decode_splitkv.restype = i
+    i64 = ctypes.c_int64
+    lib.fa_softmax_workspace_bytes.argtypes = [i64, i64, i]
+    lib.fa_softmax_workspace_bytes.restype = sz
+    lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, i, vp, sz, vp]
+    lib.fa_softmax.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -155,6 +160,53 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     if st != FA_OK:
         raise FaError(st, "fa_decode_splitkv",
                       lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_softmax_workspace_bytes(rows: int, cols: int, dtype: torch.dtype) -> int:
+    code = FA_BF16 if dtype == torch.bfloat16 else FA_F32
+    return int(load_library().fa_softmax_workspace_bytes(int(rows), int(cols), code))
+
+
+def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Row softmax and log-sum-exp through the C entry point fa_softmax.
+
+    x: [rows, cols] float32 or bfloat16; y: same shape and dtype (may be x
+    itself), or None for log-sum-exp only; lse: float32 [rows]; workspace: a
+    GPU tensor of at least fa_softmax_workspace_bytes(rows, cols, dtype) bytes
+    (None when that is 0).
+    """
+    lib = load_library()
+    _check_dev("x", x)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = x.shape
+    if y is not None:
+        _check_dev("y", y, x.dtype)
+        if y.shape != x.shape:
+            raise ValueError("y must have the shape of x")
+    _check_dev("lse", lse, torch.float32)
+    if lse.shape != (rows,):
+        raise ValueError("lse must have shape [rows]")
+    ws_bytes = 0
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_softmax(_ptr(x), _ptr(y), _ptr(lse), rows, cols, _dtype_code(x), _ptr(workspace),
+                        ws_bytes, _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def softmax(x, lse_only=False, out=None):
+    """Allocate what is needed, run fa_softmax, return (Y or None, LSE)."""
+    rows, cols = x.shape
+    y = None if lse_only else (out if out is not None else torch.empty_like(x))
+    lse = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    nbytes = fa_softmax_workspace_bytes(rows, cols, x.dtype)
+    ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=x.device) if nbytes else None
+    fa_softmax(x, y, lse, ws)
+    return y, lse
 
 
 def attention(q, k, v, scale=None, causal=False, key_lens=None):

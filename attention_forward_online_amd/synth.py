@@ -17,6 +17,13 @@ Recipe (per workload, per tensor, per batch index b):
 
 The shapes follow the problem statement of the pages: Q and O are [B, H, N, d],
 K and V are [B, H, Nk, d], LSE is [B, H, N] (decode: N = 1).
+
+Row softmax workloads (score rows of long-context attention): X is
+[rows, cols]; rows are drawn in blocks of rows, each block from its own
+derived seed, as sigma-scaled float32 normals rounded to the storage dtype;
+row r keeps a valid prefix of length len_r drawn uniformly from {0..cols} and
+holds -inf beyond it (the shape of a causal or padding mask), with len_0 =
+cols (no masked entry) and the last row's length forced to 0 (fully masked).
 """
 from __future__ import annotations
 
@@ -129,3 +136,69 @@ def random_case(B, H, N, Nk, d, dtype: torch.dtype, seed: int, device: str = "cp
     if key_lens is not None:
         kl = torch.tensor(key_lens, dtype=torch.int32, device=device)
     return {"q": q, "k": k, "v": v, "key_lens": kl}
+
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    rows: int
+    cols: int
+    dtype: str          # "f32" or "bf16"
+    sigma: float = 3.0
+    masked: bool = True  # -inf beyond a per-row valid prefix (see module doc)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def describe(self) -> str:
+        m = " valid prefix U{0..cols} (first full, last empty)" if self.masked else ""
+        return f"row softmax rows={self.rows} cols={self.cols} {self.dtype} x~N(0,{self.sigma ** 2:g}){m}"
+
+
+# Rows wider than a workgroup's on-chip share: 1024 score rows of a 256 Ki
+# context in fp32 (1 GiB in, 1 GiB out).
+SOFTMAX_WORKLOADS = {
+    w.name: w for w in [
+        SoftmaxWorkload("softmax_f32_r1024_c262144", 1024, 262144, "f32"),
+    ]
+}
+
+
+def draw_valid_lens(rows: int, cols: int, base_seed: int, name: str) -> torch.Tensor:
+    """int64 [rows]: uniform on {0..cols}; row 0 gets cols, the last row 0."""
+    g = _generator(derive_seed(base_seed, name, "valid_lens", 0), "cpu")
+    n = torch.randint(0, cols + 1, (rows,), generator=g, dtype=torch.int64)
+    n[0] = cols
+    n[rows - 1] = 0
+    return n
+
+
+def make_logits(rows: int, cols: int, dtype: torch.dtype, sigma: float, base_seed: int, name: str,
+                masked: bool = True, device: str = "cpu", gen_device: Optional[str] = None) -> torch.Tensor:
+    """[rows, cols] logits following the row-softmax recipe of the module doc."""
+    gen_device = gen_device or ("cuda" if str(device).startswith("cuda") else "cpu")
+    x = torch.empty((rows, cols), dtype=dtype, device=device)
+    if rows == 0 or cols == 0:
+        return x
+    block = max(1, (1 << 22) // cols)
+    for r0 in range(0, rows, block):
+        r1 = min(rows, r0 + block)
+        g = _generator(derive_seed(base_seed, name, "x", r0), gen_device)
+        v = torch.randn((r1 - r0, cols), generator=g, device=gen_device, dtype=torch.float32)
+        if sigma != 1.0:
+            v.mul_(sigma)
+        x[r0:r1].copy_(v.to(dtype))
+    if masked:
+        n = draw_valid_lens(rows, cols, base_seed, name).to(device)
+        pos = torch.arange(cols, device=device)
+        for r0 in range(0, rows, block):
+            r1 = min(rows, r0 + block)
+            x[r0:r1].masked_fill_(pos[None, :] >= n[r0:r1, None], float("-inf"))
+    return x
+
+
+def make_softmax_input(w: SoftmaxWorkload, base_seed: int = 0, device: str = "cpu",
+                       gen_device: Optional[str] = None) -> torch.Tensor:
+    return make_logits(w.rows, w.cols, w.torch_dtype, w.sigma, base_seed, w.name, w.masked,
+                       device, gen_device)

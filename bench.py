@@ -28,6 +28,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "fused attention fwd TFLOP/s + % bf16 MFMA peak; split-KV decode HBM GB/s"
 HEADLINE = "causal_bf16_b4h16_n2048_d64"
 DECODE = "decode_bf16_b64h32_nk16384_d128"
+SOFTMAX = "softmax_f32_r1024_c262144"
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 * 1024 * 1024   # plain copy for counter calibration
 
@@ -44,6 +45,12 @@ def decode_bytes(w):
     """Compulsory HBM bytes of one decode call: K, V, Q read; O, LSE written."""
     el = 2 if w.dtype == "bf16" else 4
     return (2 * w.B * w.H * w.Nk * w.d + 2 * w.B * w.H * w.d) * el + w.B * w.H * 4
+
+
+def softmax_bytes(w):
+    """Compulsory HBM bytes of one row-softmax call: X read once, Y and LSE written."""
+    el = 2 if w.dtype == "bf16" else 4
+    return 2 * w.rows * w.cols * el + w.rows * 4
 
 
 def time_region(fn, steps, warmup):
@@ -98,6 +105,8 @@ def main():
                     help="time only the headline prefill (used under the profiler)")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the split-KV decode (used under the profiler)")
+    ap.add_argument("--only-softmax", action="store_true",
+                    help="time only the row softmax (used under the profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE "
                          "counters scale the kernel's counters to bytes")
@@ -112,7 +121,8 @@ def main():
 
     import attention_forward_online_amd as fa
     from attention_forward_online_amd import build as fabuild
-    from attention_forward_online_amd.synth import WORKLOADS, make_inputs
+    from attention_forward_online_amd.synth import (SOFTMAX_WORKLOADS, WORKLOADS, make_inputs,
+                                                    make_softmax_input)
 
     if not os.path.exists(fabuild.LIB_PATH):
         fabuild.build()
@@ -136,9 +146,10 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
     # one fa_forward call launches exactly one kernel, so the time per step is
     # that kernel's average launch duration (plus any gap between launches)
+    side_only = args.only_decode or args.only_softmax
     ms_step = time_region(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
-                          args.steps if not args.only_decode else 1,
-                          args.warmup if not args.only_decode else 0)
+                          args.steps if not side_only else 1,
+                          args.warmup if not side_only else 0)
     flops = prefill_flops(w)
     avg_launch = ms_step
     value = flops / (ms_step * 1e-3) / 1e12
@@ -167,9 +178,9 @@ def main():
     }
     head_out = (o, lse)
 
-    if args.only_decode:
+    if side_only:
         out = {"metric": METRIC}
-    if not args.only_headline:
+    if not args.only_headline and not args.only_softmax:
         # ------------------------------------------------------------ decode
         wd = WORKLOADS[DECODE]
         di = make_inputs(wd, device=dev)
@@ -197,6 +208,29 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.only_headline and not args.only_decode:
+        # ------------------------------------------------------- row softmax
+        wsm = SOFTMAX_WORKLOADS[SOFTMAX]
+        xs = make_softmax_input(wsm, device=dev)
+        ys = torch.empty_like(xs)
+        ls = torch.empty(wsm.rows, device=dev, dtype=torch.float32)
+        nb = fa.fa_softmax_workspace_bytes(wsm.rows, wsm.cols, xs.dtype)
+        wss = torch.empty(max(nb, 16) // 4, device=dev, dtype=torch.float32)
+        ms_s = time_region(lambda: fa.fa_softmax(xs, ys, ls, wss), max(5, args.steps // 5),
+                           max(2, args.warmup // 2))
+        nbytes = softmax_bytes(wsm)
+        gbs = nbytes / (ms_s * 1e-3) / 1e9
+        out["softmax"] = {
+            "workload": wsm.describe(), "name": SOFTMAX, "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_call": round(ms_s, 4), "bytes_per_call": nbytes, "workspace_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("softmax/" + SOFTMAX),
+                         "kernels": "softmax_stats_kernel + softmax_norm_kernel"},
+        }
+        del xs, ys, ls, wss
+        torch.cuda.empty_cache()
+
+    if not args.only_headline and not args.only_decode and not args.only_softmax:
         # ------------------------------------------------- other prefill shapes
         others = {}
         for name in ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",
@@ -227,7 +261,7 @@ def main():
         out["workloads"] = others
 
     # ------------------------------------------------------- CPU oracle baseline
-    if not args.no_cpu_baseline and not args.only_decode:
+    if not args.no_cpu_baseline and not side_only:
         import oracle
         nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
         qh, kh, vh = q.cpu(), k.cpu(), v.cpu()

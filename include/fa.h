@@ -107,6 +107,44 @@ fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O
                             void *workspace, size_t workspace_bytes,
                             fa_dtype dtype, void *stream);
 
+/*
+ * Bytes of device workspace fa_softmax needs for a [rows, cols] matrix of
+ * `dtype`: 0 when every row fits one workgroup's chunk (no workspace is
+ * read), else 8 bytes per (row, chunk) for the chunk statistics.  Returns 0
+ * for invalid arguments.
+ */
+size_t fa_softmax_workspace_bytes(int64_t rows, int64_t cols, fa_dtype dtype);
+
+/*
+ * Row softmax and log-sum-exp of a matrix, streamed for rows of any width
+ * ('Online Softmax' (research-hub concept page), "Why it matters": the same
+ * running (max, sum) pair lets softmax stream rows too wide for on-chip
+ * memory; 'Online softmax in attention -- why and how', the textbook
+ * two-pass softmax and its one-pass online form).
+ *   For every row r < rows, over the entries x = X[r, 0:cols]:
+ *     m = max_j x_j,  l = sum_j exp(x_j - m),
+ *     Y[r, j] = exp(x_j - m) / l,  LSE[r] = m + ln l.
+ *   -inf entries are masked (they get y = 0); a row with no finite entry, or
+ *   cols == 0, gives Y = 0 and LSE = -inf, never NaN.  Entries must be finite
+ *   or -inf (+inf or NaN give unspecified values in that row).
+ *   X, Y: device, row-major [rows, cols], element type `dtype` (fp32, or bf16
+ *   rounded to nearest even on output), 16-byte aligned base; rows may start
+ *   anywhere.  Y == X (in place) is allowed, other overlap is not.  Y may be
+ *   NULL: only LSE is computed and X is read once.
+ *   LSE: device fp32 [rows], 4-byte aligned.
+ *   Rows whose chunk fits one workgroup read X once; wider rows take a
+ *   statistics pass that writes one (m, l) per chunk to the workspace and a
+ *   second pass that merges a row's pairs with the associative merge of
+ *   fa_decode_splitkv in a fixed order (deterministic) and writes Y.
+ *   workspace: device, 16-byte aligned, at least
+ *   fa_softmax_workspace_bytes(rows, cols, dtype) bytes (may be NULL when
+ *   that is 0); contents on entry do not matter.  Calls sharing a workspace
+ *   must not overlap in time.
+ *   Limits: cols <= 2^30, rows * cols <= 2^46; rows == 0: FA_OK, no launch.
+ */
+fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t cols,
+                     fa_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_str(fa_status status);
 

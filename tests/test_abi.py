@@ -127,6 +127,50 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == fa.FA_OK
 
 
+def test_softmax_workspace_bytes(lib):
+    f32, bf = fa.FA_F32, fa.FA_BF16
+    # rows that fit one workgroup's chunk need no workspace
+    assert lib.fa_softmax_workspace_bytes(100, 1, f32) == 0
+    assert lib.fa_softmax_workspace_bytes(100, 8192, f32) == 0
+    assert lib.fa_softmax_workspace_bytes(100, 8192, bf) == 0
+    assert lib.fa_softmax_workspace_bytes(100, 8185, bf) == 0
+    assert lib.fa_softmax_workspace_bytes(100, 8186, bf) == 100 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(5, 0, f32) == 0
+    # wider rows: one 8-byte (m, l) pair per (row, chunk); a row that does not
+    # start on a 16-byte boundary may need one more chunk
+    assert lib.fa_softmax_workspace_bytes(1024, 262144, f32) == 1024 * 32 * 8
+    assert lib.fa_softmax_workspace_bytes(7, 8193, f32) == 7 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(3, 16381, f32) == 3 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(3, 16384, f32) == 3 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(3, 16385, f32) == 3 * 3 * 8
+    assert lib.fa_softmax_workspace_bytes(2, 16385, bf) == 2 * 3 * 8
+    assert lib.fa_softmax_workspace_bytes(2, 16384, bf) == 2 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(-1, 10, f32) == 0
+    assert lib.fa_softmax_workspace_bytes(1, -1, f32) == 0
+    assert lib.fa_softmax_workspace_bytes(1, 10, 7) == 0
+
+
+def smx(lib, X=P, Y=P, LSE=P, rows=4, cols=100000, dtype=fa.FA_F32, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_softmax_workspace_bytes(rows, cols, dtype)
+    return lib.fa_softmax(X, Y, LSE, rows, cols, dtype, ws, ws_bytes, None)
+
+
+def test_softmax_rejects_bad_arguments(lib):
+    bad = fa.FA_ERR_INVALID_ARG
+    assert smx(lib, dtype=2) == bad
+    assert smx(lib, rows=-1) == bad and smx(lib, cols=-1) == bad
+    assert smx(lib, LSE=None) == bad and smx(lib, LSE=P + 2) == bad
+    assert smx(lib, X=None) == bad and smx(lib, X=P + 4) == bad
+    assert smx(lib, Y=P + 8) == bad
+    assert smx(lib, ws=None) == bad and smx(lib, ws=P + 8) == bad
+    assert smx(lib, ws_bytes=lib.fa_softmax_workspace_bytes(4, 100000, fa.FA_F32) - 8) == bad
+    assert smx(lib, cols=(1 << 30) + 1, ws_bytes=1 << 40) == bad
+    assert smx(lib, rows=1 << 20, cols=1 << 27, ws_bytes=1 << 40) == bad
+    # nothing to do: no launch, no pointer is looked at
+    assert smx(lib, X=None, Y=None, LSE=None, ws=None, rows=0) == fa.FA_OK
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         fa.load_library(str(tmp_path / "libfa.so"))
