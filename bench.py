@@ -225,7 +225,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("softmax/" + SOFTMAX),
-                         "kernels": "softmax_stats_kernel + softmax_norm_kernel"},
+                         "kernels": "softmax_reset_kernel + softmax_coop_kernel (one pass over X)"},
         }
         del xs, ys, ls, wss
         torch.cuda.empty_cache()

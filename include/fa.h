@@ -132,10 +132,14 @@ size_t fa_softmax_workspace_bytes(int64_t rows, int64_t cols, fa_dtype dtype);
  *   anywhere.  Y == X (in place) is allowed, other overlap is not.  Y may be
  *   NULL: only LSE is computed and X is read once.
  *   LSE: device fp32 [rows], 4-byte aligned.
- *   Rows whose chunk fits one workgroup read X once; wider rows take a
- *   statistics pass that writes one (m, l) per chunk to the workspace and a
- *   second pass that merges a row's pairs with the associative merge of
- *   fa_decode_splitkv in a fixed order (deterministic) and writes Y.
+ *   X is read once when a row fits one workgroup (8192 elements) and, out of
+ *   place, for rows of up to 2^21 fp32 / 2^22 bf16 elements: the workgroups
+ *   of a row's 64 KiB chunks keep their chunk in registers, exchange their
+ *   (m, l) pairs through the workspace and merge them with the associative
+ *   merge of fa_decode_splitkv in a fixed order.  LSE-only calls, in-place
+ *   calls and wider rows take two passes: one (m, l) per chunk to the
+ *   workspace, then the merge and the normalisation.  Results are
+ *   deterministic for a given call form.
  *   workspace: device, 16-byte aligned, at least
  *   fa_softmax_workspace_bytes(rows, cols, dtype) bytes (may be NULL when
  *   that is 0); contents on entry do not matter.  Calls sharing a workspace

@@ -127,6 +127,10 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == fa.FA_OK
 
 
+def wsz(rows, chunks):
+    return 16 + rows * chunks * 8
+
+
 def test_softmax_workspace_bytes(lib):
     f32, bf = fa.FA_F32, fa.FA_BF16
     # rows that fit one workgroup's chunk need no workspace
@@ -134,17 +138,18 @@ def test_softmax_workspace_bytes(lib):
     assert lib.fa_softmax_workspace_bytes(100, 8192, f32) == 0
     assert lib.fa_softmax_workspace_bytes(100, 8192, bf) == 0
     assert lib.fa_softmax_workspace_bytes(100, 8185, bf) == 0
-    assert lib.fa_softmax_workspace_bytes(100, 8186, bf) == 100 * 2 * 8
+    assert lib.fa_softmax_workspace_bytes(100, 8186, bf) == wsz(100, 2)
     assert lib.fa_softmax_workspace_bytes(5, 0, f32) == 0
-    # wider rows: one 8-byte (m, l) pair per (row, chunk); a row that does not
-    # start on a 16-byte boundary may need one more chunk
-    assert lib.fa_softmax_workspace_bytes(1024, 262144, f32) == 1024 * 32 * 8
-    assert lib.fa_softmax_workspace_bytes(7, 8193, f32) == 7 * 2 * 8
-    assert lib.fa_softmax_workspace_bytes(3, 16381, f32) == 3 * 2 * 8
-    assert lib.fa_softmax_workspace_bytes(3, 16384, f32) == 3 * 2 * 8
-    assert lib.fa_softmax_workspace_bytes(3, 16385, f32) == 3 * 3 * 8
-    assert lib.fa_softmax_workspace_bytes(2, 16385, bf) == 2 * 3 * 8
-    assert lib.fa_softmax_workspace_bytes(2, 16384, bf) == 2 * 2 * 8
+    # wider rows: a 16-byte header (a counter), then one 8-byte (m, l) pair per
+    # (row, 8192-element chunk); a row that does not start on a 16-byte
+    # boundary may need one more chunk
+    assert lib.fa_softmax_workspace_bytes(1024, 262144, f32) == wsz(1024, 32)
+    assert lib.fa_softmax_workspace_bytes(7, 8193, f32) == wsz(7, 2)
+    assert lib.fa_softmax_workspace_bytes(3, 16381, f32) == wsz(3, 2)
+    assert lib.fa_softmax_workspace_bytes(3, 16384, f32) == wsz(3, 2)
+    assert lib.fa_softmax_workspace_bytes(3, 16385, f32) == wsz(3, 3)
+    assert lib.fa_softmax_workspace_bytes(2, 16385, bf) == wsz(2, 3)
+    assert lib.fa_softmax_workspace_bytes(2, 16384, bf) == wsz(2, 2)
     assert lib.fa_softmax_workspace_bytes(-1, 10, f32) == 0
     assert lib.fa_softmax_workspace_bytes(1, -1, f32) == 0
     assert lib.fa_softmax_workspace_bytes(1, 10, 7) == 0

@@ -149,13 +149,26 @@ def test_lse_only_and_in_place(dtype, cols):
     bits = (lambda t: t.view(torch.int16)) if dtype == torch.bfloat16 else (lambda t: t)
     assert torch.equal(bits(to_host(x)), bits(xh))
     y_sep, lse_sep = run(x)
+    check_rows(xh, None, lse_only, f"lse-only {dtype} {cols}", dtype)
+    check_rows(xh, y_sep, lse_sep, f"separate {dtype} {cols}", dtype)
     y_in, lse_in = run(x, out=x)          # y written over x
     assert y_in.data_ptr() == x.data_ptr()
     check_rows(xh, y_in, lse_in, f"in-place {dtype} {cols}", dtype)
-    # same bits whichever way the call is made
-    assert torch.equal(to_host(lse_only), to_host(lse_sep))
-    assert torch.equal(to_host(lse_in), to_host(lse_sep))
-    assert torch.equal(bits(to_host(y_in)), bits(to_host(y_sep)))
+
+    # paths that cut the row into the same chunks give the same bits: rows
+    # that fit one workgroup take one kernel every way; wider rows take the
+    # two-pass kernels for lse only and in place (8192-element chunks) and the
+    # one-pass kernel out of place (64 KiB chunks), equal to the others only
+    # up to rounding
+    def same(a, b, what):
+        a, b = to_host(a), to_host(b)
+        bad = (a != b) & ~(torch.isneginf(a) & torch.isneginf(b))
+        assert not bad.any(), (f"{what}: rows {torch.nonzero(bad).flatten().tolist()} differ: "
+                               f"{a[bad].tolist()} vs {b[bad].tolist()}")
+    same(lse_only, lse_in, "lse-only vs in place")
+    if cols + 7 <= 8192:
+        same(lse_only, lse_sep, "lse-only vs separate")
+        assert torch.equal(bits(to_host(y_in)), bits(to_host(y_sep)))
 
 
 def test_empty_shapes():
@@ -169,16 +182,20 @@ def test_empty_shapes():
 
 
 def test_deterministic_and_row_blocks():
-    # 80 rows of 1 MiB: the two-pass path runs in more than one block of rows
+    # 80 rows of 1 MiB.  Out of place: the one-pass path, twice, bit-identical.
+    # In place: the two-pass path over more than one block of rows (64 MiB
+    # each)
     rows, cols = 80, 262144
     x = case(rows, cols, torch.float32, seed=3)
-    say(f"[gpu] fa_softmax row blocks rows={rows} cols={cols}")
+    say(f"[gpu] fa_softmax one-pass / row blocks rows={rows} cols={cols}")
     y1, l1 = run(x)
     y2, l2 = run(x)
     assert torch.equal(to_host(y1), to_host(y2)) and torch.equal(to_host(l1), to_host(l2))
+    xh = to_host(x)
+    y3, l3 = run(x, out=x)
     pick = [0, 1, 31, 63, 64, 65, 78, 79]
-    xh = to_host(x)[pick]
-    check_rows(xh, to_host(y1)[pick], to_host(l1)[pick], "row blocks", torch.float32)
+    check_rows(xh[pick], to_host(y1)[pick], to_host(l1)[pick], "one-pass", torch.float32)
+    check_rows(xh[pick], to_host(y3)[pick], to_host(l3)[pick], "row blocks in place", torch.float32)
 
 
 @pytest.mark.parametrize("name", sorted(synth.SOFTMAX_WORKLOADS))
@@ -203,3 +220,21 @@ def test_full_size_workload(name):
     assert torch.all(d <= 1e-5 + 2.4e-7 * ref[has].abs())
     assert torch.all(torch.isneginf(lse[~has]))
     assert torch.all(y[~fin] == 0)
+
+
+def test_workspace_reuse_across_calls():
+    # one workspace for several calls in a row (one-pass wide path, then the
+    # two-pass in-place path, then one-pass again): every call resets what it
+    # reads, so each result matches the oracle
+    rows, cols = 6, 50000
+    nbytes = fa.fa_softmax_workspace_bytes(rows, cols, torch.float32)
+    ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=DEV)
+    for k, in_place in enumerate((False, True, False, False)):
+        x = case(rows, cols, torch.float32, seed=10 + k)
+        xh = to_host(x).clone()
+        y = x if in_place else torch.empty_like(x)
+        say(f"[gpu] fa_softmax reused workspace call {k} in_place={in_place}")
+        fa.fa_softmax(x, y, lse, ws)
+        torch.cuda.synchronize()
+        check_rows(xh, y, lse, f"reuse {k}", torch.float32)
