@@ -6,9 +6,9 @@ include/fa.h); this package only marshals torch tensors into that ABI.
 from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_F32,
                  FA_OK, FaError, attention, decode, fa_decode_splitkv, fa_decode_workspace_bytes,
                  fa_forward, fa_softmax, fa_softmax_workspace_bytes, load_library, softmax,
-                 status_str)
+                 status_str, testing_set_softmax_spin_limit)
 
 __all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_F32",
            "FA_OK", "FaError", "attention", "decode", "fa_decode_splitkv",
            "fa_decode_workspace_bytes", "fa_forward", "fa_softmax", "fa_softmax_workspace_bytes",
-           "load_library", "softmax", "status_str"]
+           "load_library", "softmax", "status_str", "testing_set_softmax_spin_limit"]

@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_kernels.h"
+#include "fa_testing.h"
 
 namespace {
 
@@ -132,5 +133,7 @@ fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t c
     fa::SoftmaxArgs a{X, Y, LSE, rows, cols, workspace};
     return from_hip(fa::launch_softmax(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
 }
+
+void fa_testing_set_softmax_spin_limit(int limit) { fa::set_softmax_spin_limit(limit); }
 
 }  // extern "C"

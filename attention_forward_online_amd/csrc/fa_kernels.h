@@ -47,5 +47,7 @@ hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
 // Row softmax / log-sum-exp of a [rows, cols] fp32 or bf16 matrix.
 size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16);
 hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream);
+// Test hook: polls of the one-pass wait before its fallback (< 0: default).
+void set_softmax_spin_limit(int limit);
 
 }  // namespace fa

@@ -157,6 +157,7 @@ struct Params {
     long long cols;
     long long total_bytes;  // rows * cols * sizeof(T)
     int S;                  // chunks per row
+    int spin_limit;         // one-pass wait: polls before the fallback
     int grid_chunks;        // chunk slots per row in this grid (S, or 1 when only lse is written)
 };
 
@@ -366,6 +367,8 @@ constexpr int kCoopMaxChunks = 128;
 template <typename T> constexpr int coop_nv() { return 64 * 1024 / (kThreads * 16); }
 template <typename T> constexpr int coop_chunk() { return kThreads * coop_nv<T>() * Elem<T>::kVec; }
 constexpr int kSpinLimit = 1 << 16;        // polls before the fallback (about 0.1 s)
+// Polls of the next one-pass launches; only the test hook changes it.
+int g_spin_limit = kSpinLimit;
 constexpr float kUnset = -1.f;
 
 __device__ __forceinline__ uint64_t pack_ml(ML s) {
@@ -424,7 +427,7 @@ __device__ ML stream_row_stats(const Params &p, long long r, ML *sh) {
 // own row; every earlier row has all its chunks held by resident workgroups
 // that do not wait on later tickets, so the wait ends whenever the chip holds
 // one row's chunks at once (S <= 128 here, against 1280 resident workgroups
-// at 5 per CU).  The wait is still bounded: past kSpinLimit polls the
+// at 5 per CU).  The wait is still bounded: past the poll limit the
 // workgroup streams the row itself (same result up to rounding order), so
 // every wave exits.  X must not alias Y on this path (the fallback re-reads X).
 template <typename T>
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void softmax_coop_kernel(Params p) {
     // (each pair is one 64-bit atomic: the sentinel or the whole pair)
     ML mine{neg_inf(), 0.f};
     bool ready = false;
-    for (int it = 0; it < kSpinLimit; ++it) {
+    for (int it = 0; it < p.spin_limit; ++it) {
         int ok = 1;
         if ((int)threadIdx.x < p.S) {
             mine = unpack_ml(__hip_atomic_load(slots + threadIdx.x, __ATOMIC_RELAXED,
@@ -555,6 +558,7 @@ hipError_t launch_softmax_t(const SoftmaxArgs &a, hipStream_t stream) {
     p.X = static_cast<const uint8_t *>(a.X);
     p.Y = static_cast<uint8_t *>(a.Y);
     p.LSE = a.LSE;
+    p.spin_limit = g_spin_limit;
     p.ticket = static_cast<unsigned *>(a.workspace);
     p.ws = reinterpret_cast<f32x2_t *>(static_cast<uint8_t *>(a.workspace) + kWsHeader);
     p.cols = a.cols;
@@ -647,6 +651,8 @@ hipError_t launch_softmax_t(const SoftmaxArgs &a, hipStream_t stream) {
 size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16) {
     return is_bf16 ? workspace_bytes_t<uint16_t>(rows, cols) : workspace_bytes_t<float>(rows, cols);
 }
+
+void set_softmax_spin_limit(int limit) { g_spin_limit = limit < 0 ? kSpinLimit : limit; }
 
 hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream) {
     return is_bf16 ? launch_softmax_t<uint16_t>(a, stream) : launch_softmax_t<float>(a, stream);

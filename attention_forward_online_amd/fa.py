@@ -54,6 +54,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_softmax_workspace_bytes.restype = sz
     lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, i, vp, sz, vp]
     lib.fa_softmax.restype = i
+    lib.fa_testing_set_softmax_spin_limit.argtypes = [i]
+    lib.fa_testing_set_softmax_spin_limit.restype = None
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -196,6 +198,13 @@ def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
                         ws_bytes, _stream_handle(stream))
     if st != FA_OK:
         raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def testing_set_softmax_spin_limit(limit: int) -> None:
+    """Test hook (include/fa_testing.h): polls of the one-pass softmax wait
+    before its fallback; 0 forces the fallback, a negative value restores the
+    default."""
+    load_library().fa_testing_set_softmax_spin_limit(int(limit))
 
 
 def softmax(x, lse_only=False, out=None):

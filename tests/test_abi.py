@@ -44,6 +44,17 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name)
 
 
+def test_testing_header_symbols_are_exported(lib):
+    text = open(os.path.join(ROOT, "include", "fa_testing.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*void\s+(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    assert names == ["fa_testing_set_softmax_spin_limit"]
+    out = subprocess.run(["nm", "-D", "--defined-only", fabuild.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "fa_testing_set_softmax_spin_limit" in out
+    lib.fa_testing_set_softmax_spin_limit(-1)   # host-only: no device work
+
+
 def test_status_strings(lib):
     assert fa.status_str(fa.FA_OK) == "FA_OK"
     assert fa.status_str(fa.FA_ERR_INVALID_ARG) == "FA_ERR_INVALID_ARG"

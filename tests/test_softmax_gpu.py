@@ -238,3 +238,21 @@ def test_workspace_reuse_across_calls():
         fa.fa_softmax(x, y, lse, ws)
         torch.cuda.synchronize()
         check_rows(xh, y, lse, f"reuse {k}", torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_one_pass_wait_fallback(dtype):
+    # forced from the host: with a poll limit of 0 every workgroup of the
+    # one-pass kernel computes its row's statistics by streaming the row
+    # itself; the result still matches the oracle
+    rows, cols = 5, 70001
+    x = case(rows, cols, dtype, seed=21)
+    say(f"[gpu] fa_softmax one-pass fallback {dtype} rows={rows} cols={cols}")
+    fa.testing_set_softmax_spin_limit(0)
+    try:
+        y, lse = run(x)
+    finally:
+        fa.testing_set_softmax_spin_limit(-1)
+    check_rows(to_host(x), y, lse, f"fallback {dtype}", dtype)
+    y2, lse2 = run(x)
+    check_rows(to_host(x), y2, lse2, f"after fallback {dtype}", dtype)
