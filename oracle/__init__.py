@@ -51,6 +51,12 @@ def load(path: str = _LIB_PATH, rebuild_if_missing: bool = True):
     lib.oracle_softmax_rows_f64.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_long,
                                             ctypes.c_long, ctypes.c_void_p, dp]
     lib.oracle_softmax_rows_f64.restype = ctypes.c_int
+    lib.oracle_attention_backward_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
+        dp, dp, dp, ctypes.c_int]
+    lib.oracle_attention_backward_f64.restype = ctypes.c_int
     return lib
 
 
@@ -170,3 +176,53 @@ def softmax_rows(x, want_y=True, lib=None):
     if rc != 0:
         raise RuntimeError(f"oracle_softmax_rows_f64 returned {rc}")
     return Y, LSE
+
+
+def attention_backward(q, k, v, do, scale=None, causal=False, key_lens=None, heads=None,
+                       nthreads=None, lib=None):
+    """fp64 gradients (dQ, dK, dV) of L = sum(dO * O) for O = attention(q, k, v).
+
+    q, do: [B,H,N,d]; k, v: [B,H,Nk,d] (one dtype); heads: flat b*H + h
+    indices to compute (None = all).  Returns float64 arrays shaped like the
+    inputs when heads is None, else [len(heads), N|Nk, d].
+    """
+    lib = lib or _get()
+    qa, dt = _host_array(q)
+    ka, dtk = _host_array(k)
+    va, dtv = _host_array(v)
+    da, dtd = _host_array(do)
+    if not (dt == dtk == dtv == dtd):
+        raise TypeError("q, k, v and do must share one dtype")
+    B, H, N, d = qa.shape
+    Nk = ka.shape[2]
+    if ka.shape != (B, H, Nk, d) or va.shape != (B, H, Nk, d) or da.shape != qa.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kl = None
+    if key_lens is not None:
+        kl = np.ascontiguousarray(np.asarray(
+            key_lens.cpu().numpy() if hasattr(key_lens, "cpu") else key_lens, dtype=np.int32))
+        if kl.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
+    if heads is None:
+        nh, hidx = B * H, None
+    else:
+        hidx = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+        nh = hidx.size
+    dQ = np.zeros((nh, N, d))
+    dK = np.zeros((nh, Nk, d))
+    dV = np.zeros((nh, Nk, d))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.oracle_attention_backward_f64(
+        qa.ctypes.data, ka.ctypes.data, va.ctypes.data, da.ctypes.data, dt, B, H, N, Nk, d,
+        float(scale), int(bool(causal)), kl.ctypes.data if kl is not None else None, nh,
+        hidx.ctypes.data if hidx is not None else None,
+        dQ.ctypes.data_as(dp), dK.ctypes.data_as(dp), dV.ctypes.data_as(dp), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_backward_f64 returned {rc}")
+    if heads is None:
+        return dQ.reshape(B, H, N, d), dK.reshape(B, H, Nk, d), dV.reshape(B, H, Nk, d)
+    return dQ, dK, dV

@@ -40,6 +40,18 @@
  * softmax / log-sum-exp kernel ('Online Softmax' research-hub page, "Why it
  * matters": the recurrence also streams rows too wide for on-chip memory).
  *
+ * The backward pass (oracle_attention_backward_f64) is the exact gradient of
+ * the forward above for a loss L = sum dO . O, written out by the chain rule
+ * ('Online softmax in attention -- why and how', "Where this is heading":
+ * backward recomputes the scores from the cached row statistics; the
+ * gradient itself is plain calculus of the same definition):
+ *     P = softmax rows of the visible scores, O = P V,
+ *     D_i = dO_i . O_i,  dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i),
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ *     dV_j = sum_i P_ij dO_i,
+ * with masked (query, key) pairs contributing nothing; a row with no visible
+ * key has P = 0 and dQ_i = 0.  Pinned by central differences of the forward.
+ *
  * Parity pins (tests/test_oracle.py): the worked softmax examples printed on
  * the pages, the chunk-merge invariant of 'Online Softmax & FlashAttention'
  * Step 1, the tiled V1 shapes of its Step 2, closed forms, invariants and a
@@ -288,6 +300,189 @@ int oracle_attention_f64(const void *Q, const void *K, const void *V, int dtype,
             pthread_join(tids[t], NULL);
         else
             attend_job(&jobs[t]);           /* no thread: run it here */
+    }
+    for (t = 0; t < nthreads; ++t)
+        if (jobs[t].status != 0)
+            status = jobs[t].status;
+    free(jobs);
+    free(tids);
+    free(started);
+    return status;
+}
+
+/* ------------------------------------------------------------- backward */
+
+typedef struct {
+    const void *Q, *K, *V, *dO;
+    int dtype;
+    long B, H, N, Nk, d;
+    double scale;
+    int causal;
+    const int32_t *key_lens;
+    const int64_t *heads;       /* flat b*H + h, or NULL = all */
+    double *dQ, *dK, *dV;       /* [nheads, N, d], [nheads, Nk, d] x 2 */
+} bwd_args;
+
+typedef struct {
+    const bwd_args *a;
+    long begin, end;            /* range of heads (indices into the head list) */
+    int status;
+} bwd_job;
+
+/* Gradients of one head: row by row, the row's softmax (three passes), its
+ * output, then the chain rule for that row's contributions. */
+static void backward_head(const bwd_args *a, long hidx, double *s, double *p, double *o)
+{
+    long bh = a->heads ? (long)a->heads[hidx] : hidx;
+    long b = bh / a->H, d = a->d, N = a->N, Nk = a->Nk, i, j, c;
+    size_t qbase = (size_t)bh * N * d, kvbase = (size_t)bh * Nk * d;
+    double *dQ = a->dQ + (size_t)hidx * N * d;
+    double *dK = a->dK + (size_t)hidx * Nk * d;
+    double *dV = a->dV + (size_t)hidx * Nk * d;
+    attn_args va;               /* only the fields visible_keys reads */
+
+    memset(&va, 0, sizeof va);
+    va.N = N; va.Nk = Nk; va.causal = a->causal; va.key_lens = a->key_lens;
+    for (c = 0; c < N * d; ++c)
+        dQ[c] = 0.0;
+    for (c = 0; c < Nk * d; ++c) {
+        dK[c] = 0.0;
+        dV[c] = 0.0;
+    }
+    for (i = 0; i < N; ++i) {
+        long nvis = visible_keys(&va, b, i);
+        size_t qo = qbase + (size_t)i * d;
+        double m = -INFINITY, l = 0.0, D = 0.0;
+        if (nvis == 0)
+            continue;                       /* P = 0: no gradient through this row */
+        for (j = 0; j < nvis; ++j) {        /* scores */
+            double dot = 0.0;
+            for (c = 0; c < d; ++c)
+                dot += widen(a->Q, a->dtype, qo + c) * widen(a->K, a->dtype, kvbase + (size_t)j * d + c);
+            s[j] = dot * a->scale;
+        }
+        for (j = 0; j < nvis; ++j)          /* pass 1 */
+            if (s[j] > m)
+                m = s[j];
+        for (j = 0; j < nvis; ++j)          /* pass 2 */
+            l = l + exp(s[j] - m);
+        for (c = 0; c < d; ++c)
+            o[c] = 0.0;
+        for (j = 0; j < nvis; ++j) {        /* pass 3: P and O = P V */
+            p[j] = exp(s[j] - m) / l;
+            for (c = 0; c < d; ++c)
+                o[c] += p[j] * widen(a->V, a->dtype, kvbase + (size_t)j * d + c);
+        }
+        for (c = 0; c < d; ++c)             /* D_i = dO_i . O_i */
+            D += widen(a->dO, a->dtype, qo + c) * o[c];
+        for (j = 0; j < nvis; ++j) {
+            size_t ko = kvbase + (size_t)j * d;
+            double dp = 0.0, ds;
+            for (c = 0; c < d; ++c)         /* dP_ij = dO_i . v_j */
+                dp += widen(a->dO, a->dtype, qo + c) * widen(a->V, a->dtype, ko + c);
+            ds = p[j] * (dp - D);
+            for (c = 0; c < d; ++c) {
+                dQ[(size_t)i * d + c] += a->scale * ds * widen(a->K, a->dtype, ko + c);
+                dK[(size_t)j * d + c] += a->scale * ds * widen(a->Q, a->dtype, qo + c);
+                dV[(size_t)j * d + c] += p[j] * widen(a->dO, a->dtype, qo + c);
+            }
+        }
+    }
+}
+
+static void *backward_job(void *arg)
+{
+    bwd_job *job = (bwd_job *)arg;
+    const bwd_args *a = job->a;
+    size_t nk = (size_t)(a->Nk > 0 ? a->Nk : 1);
+    double *s = (double *)malloc(sizeof(double) * nk);
+    double *p = (double *)malloc(sizeof(double) * nk);
+    double *o = (double *)malloc(sizeof(double) * (size_t)a->d);
+    long h;
+    if (!s || !p || !o) {
+        free(s);
+        free(p);
+        free(o);
+        job->status = -2;
+        return NULL;
+    }
+    for (h = job->begin; h < job->end; ++h)
+        backward_head(a, h, s, p, o);
+    free(s);
+    free(p);
+    free(o);
+    job->status = 0;
+    return NULL;
+}
+
+/*
+ * Attention backward in fp64: dQ, dK, dV of L = sum dO . O for the forward of
+ * oracle_attention_f64 (same masking rules), for every head (heads == NULL,
+ * nheads must be B*H) or for the listed flat heads b*H + h.
+ * Q, dO: [B,H,N,d]; K, V: [B,H,Nk,d]; element type `dtype` as in the forward.
+ * dQ: fp64 [nheads, N, d]; dK, dV: fp64 [nheads, Nk, d].  Returns 0, -1 for
+ * invalid arguments, -2 when memory runs out.
+ */
+int oracle_attention_backward_f64(const void *Q, const void *K, const void *V, const void *dO,
+                                  int dtype, long B, long H, long N, long Nk, long d,
+                                  double scale, int causal, const int32_t *key_lens,
+                                  long nheads, const int64_t *heads,
+                                  double *dQ, double *dK, double *dV, int nthreads)
+{
+    bwd_args a;
+    bwd_job *jobs;
+    pthread_t *tids;
+    char *started;
+    long r, per, t;
+    int status = 0;
+
+    if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0 || nheads < 0 ||
+        dtype < ORACLE_F64 || dtype > ORACLE_BF16 || (causal != 0 && causal != 1))
+        return -1;
+    if (!heads && nheads != B * H)
+        return -1;
+    if (heads)
+        for (r = 0; r < nheads; ++r)
+            if (heads[r] < 0 || heads[r] >= B * H)
+                return -1;
+    if (nheads == 0)
+        return 0;
+    if ((N > 0 && (!Q || !dO || !dQ)) || (Nk > 0 && (!K || !V || !dK || !dV)))
+        return -1;
+
+    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.dtype = dtype;
+    a.B = B; a.H = H; a.N = N; a.Nk = Nk; a.d = d;
+    a.scale = scale; a.causal = causal; a.key_lens = key_lens;
+    a.heads = heads; a.dQ = dQ; a.dK = dK; a.dV = dV;
+
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nheads)
+        nthreads = (int)nheads;
+    jobs = (bwd_job *)calloc((size_t)nthreads, sizeof *jobs);
+    tids = (pthread_t *)calloc((size_t)nthreads, sizeof *tids);
+    started = (char *)calloc((size_t)nthreads, 1);
+    if (!jobs || !tids || !started) {
+        free(jobs);
+        free(tids);
+        free(started);
+        return -2;
+    }
+    per = (nheads + nthreads - 1) / nthreads;
+    for (t = 0; t < nthreads; ++t) {
+        jobs[t].a = &a;
+        jobs[t].begin = t * per < nheads ? t * per : nheads;
+        jobs[t].end = (t + 1) * per < nheads ? (t + 1) * per : nheads;
+        jobs[t].status = -2;
+    }
+    for (t = 1; t < nthreads; ++t)
+        started[t] = pthread_create(&tids[t], NULL, backward_job, &jobs[t]) == 0;
+    backward_job(&jobs[0]);
+    for (t = 1; t < nthreads; ++t) {
+        if (started[t])
+            pthread_join(tids[t], NULL);
+        else
+            backward_job(&jobs[t]);
     }
     for (t = 0; t < nthreads; ++t)
         if (jobs[t].status != 0)

@@ -354,9 +354,132 @@ def check_softmax_rows(lib):
     assert Ye.shape == (2, 0) and np.all(Le == -np.inf)
 
 
+# --------------------------------------------------------------------- backward
+def _bwd_case(r, B, H, N, Nk, d):
+    return (r.standard_normal((B, H, N, d)), r.standard_normal((B, H, Nk, d)),
+            r.standard_normal((B, H, Nk, d)), r.standard_normal((B, H, N, d)))
+
+
+def _loss(lib, q, k, v, do, **kw):
+    O, _ = oracle.attention(q, k, v, lib=lib, nthreads=1, **kw)
+    return float((O * do).sum())
+
+
+BWD_CASES = [
+    dict(B=1, H=2, N=5, Nk=4, d=3, causal=False, key_lens=None, scale=None),
+    dict(B=2, H=1, N=4, Nk=6, d=3, causal=True, key_lens=None, scale=0.7),
+    dict(B=2, H=1, N=6, Nk=4, d=2, causal=True, key_lens=None, scale=None),   # N > Nk: rows 0, 1 see nothing
+    dict(B=2, H=1, N=4, Nk=5, d=3, causal=False, key_lens=[3, 0], scale=None),
+    dict(B=1, H=1, N=5, Nk=5, d=4, causal=True, key_lens=[4], scale=1.3),
+]
+
+
+def check_backward_finite_differences(lib):
+    # central differences of the (separately pinned) forward: L = sum dO . O
+    r = _rng(77)
+    h = 1e-5
+    for cs in BWD_CASES:
+        B, H, N, Nk, d = cs["B"], cs["H"], cs["N"], cs["Nk"], cs["d"]
+        kw = dict(scale=cs["scale"], causal=cs["causal"], key_lens=cs["key_lens"])
+        q, k, v, do = _bwd_case(r, B, H, N, Nk, d)
+        dQ, dK, dV = oracle.attention_backward(q, k, v, do, lib=lib, nthreads=1, **kw)
+        for which, g in ((0, dQ), (1, dK), (2, dV)):
+            base = [q, k, v]
+            x = base[which]
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                argp, argm = list(base), list(base)
+                argp[which], argm[which] = xp, xm
+                fd = (_loss(lib, *argp, do, **kw) - _loss(lib, *argm, do, **kw)) / (2 * h)
+                assert abs(fd - g[idx]) <= 1e-6 * (1.0 + abs(g[idx])), (cs, which, idx, fd, g[idx])
+
+
+def check_backward_torch_autograd(lib):
+    # the library's automatic differentiation of the same masked attention, fp64
+    r = _rng(78)
+    for cs in BWD_CASES:
+        B, H, N, Nk, d = cs["B"], cs["H"], cs["N"], cs["Nk"], cs["d"]
+        scale = cs["scale"] if cs["scale"] is not None else 1.0 / math.sqrt(d)
+        q, k, v, do = _bwd_case(r, B, H, N, Nk, d)
+        dQ, dK, dV = oracle.attention_backward(q, k, v, do, scale=scale, causal=cs["causal"],
+                                               key_lens=cs["key_lens"], lib=lib)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+        vis = torch.ones(B, 1, N, Nk, dtype=torch.bool)
+        if cs["causal"]:
+            i = torch.arange(N)[:, None]
+            j = torch.arange(Nk)[None, :]
+            vis = vis & (j <= i + (Nk - N))
+        if cs["key_lens"] is not None:
+            kl = torch.tensor(cs["key_lens"])[:, None, None, None]
+            vis = vis & (torch.arange(Nk)[None, None, None, :] < kl)
+        s = s.masked_fill(~vis, float("-inf"))
+        any_vis = vis.any(dim=-1, keepdim=True)
+        p = torch.where(any_vis, torch.softmax(torch.where(any_vis, s, torch.zeros_like(s)), dim=-1),
+                        torch.zeros_like(s))
+        o = torch.matmul(p, tv)
+        (o * torch.from_numpy(do)).sum().backward()
+        for g, t in ((dQ, tq), (dK, tk), (dV, tv)):
+            assert np.allclose(g, t.grad.numpy(), rtol=0, atol=1e-12), cs
+
+
+def check_backward_closed_forms(lib):
+    r = _rng(79)
+    # one key: softmax is constant 1, so no gradient reaches Q or K; dV = sum of dO
+    q, k, v, do = _bwd_case(r, 1, 2, 6, 1, 4)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, lib=lib)
+    assert np.abs(dQ).max() <= 1e-14 and np.abs(dK).max() <= 1e-14
+    assert np.allclose(dV[:, :, 0], do.sum(axis=2), rtol=0, atol=1e-13)
+    # identical value rows: O = v whatever P is, so dS = 0
+    q, k, v, do = _bwd_case(r, 1, 1, 5, 7, 3)
+    v[:] = v[:, :, :1, :]
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, lib=lib)
+    assert np.abs(dQ).max() <= 1e-13 and np.abs(dK).max() <= 1e-13
+    # zero upstream gradient
+    dQ, dK, dV = oracle.attention_backward(q, k, v, np.zeros_like(do), lib=lib)
+    assert not dQ.any() and not dK.any() and not dV.any()
+    # invariants: key shift leaves every softmax unchanged, so sum_j dK_j = 0;
+    # a value shift moves every visible row's output, so sum_j dV_j = sum_i dO_i
+    for cs in BWD_CASES:
+        q, k, v, do = _bwd_case(r, cs["B"], cs["H"], cs["N"], cs["Nk"], cs["d"])
+        kw = dict(scale=cs["scale"], causal=cs["causal"], key_lens=cs["key_lens"])
+        dQ, dK, dV = oracle.attention_backward(q, k, v, do, lib=lib, **kw)
+        _, L = oracle.attention(q, k, v, lib=lib, **kw)
+        seen = np.isfinite(L)[..., None]
+        assert np.abs(dK.sum(axis=2)).max() <= 1e-12, cs
+        assert np.allclose(dV.sum(axis=2), (do * seen).sum(axis=2), rtol=0, atol=1e-12), cs
+        assert np.all(dQ[~np.isfinite(L)] == 0.0), cs
+    # Nk = 0: nothing is visible
+    q, k, v, do = _bwd_case(r, 1, 1, 3, 0, 2)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, lib=lib)
+    assert not dQ.any() and dK.shape == (1, 1, 0, 2)
+
+
+def check_backward_heads_and_widening(lib):
+    r = _rng(80)
+    q, k, v, do = _bwd_case(r, 2, 3, 7, 9, 4)
+    full = oracle.attention_backward(q, k, v, do, causal=True, key_lens=[9, 4], lib=lib)
+    sub = oracle.attention_backward(q, k, v, do, causal=True, key_lens=[9, 4], heads=[4, 0], lib=lib)
+    for f, s_ in zip(full, sub):
+        fl = f.reshape(6, *f.shape[2:])
+        assert np.array_equal(s_[0], fl[4]) and np.array_equal(s_[1], fl[0])
+    # bf16 and fp32 storage widen exactly: same result as the widened fp64 values
+    tb = [torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v, do)]
+    gb = oracle.attention_backward(*tb, scale=0.5, lib=lib)
+    g64 = oracle.attention_backward(*[t.double().numpy() for t in tb], scale=0.5, lib=lib)
+    assert all(np.array_equal(a, b) for a, b in zip(gb, g64))
+    tf = [x.astype(np.float32) for x in (q, k, v, do)]
+    gf = oracle.attention_backward(*tf, scale=0.5, lib=lib)
+    g64 = oracle.attention_backward(*[x.astype(np.float64) for x in tf], scale=0.5, lib=lib)
+    assert all(np.array_equal(a, b) for a, b in zip(gf, g64))
+
+
 ALL_CHECKS = [
     check_worked_example, check_four_element, check_x153, check_chunk_merge,
     check_merge_guard_negative_control, check_tiled_shapes, check_closed_forms,
     check_invariants, check_torch_sdpa, check_bf16_widening, check_rows_and_threads,
-    check_softmax_rows,
+    check_softmax_rows, check_backward_finite_differences, check_backward_torch_autograd,
+    check_backward_closed_forms, check_backward_heads_and_widening,
 ]

@@ -31,6 +31,19 @@ MUTANTS = {
     "masked_row_lse_zero": ("a->LSE[out_row] = -INFINITY;\n        return;", "a->LSE[out_row] = 0.0;\n        return;"),
     "rows_lse_drops_max": ("LSE[r] = l > 0.0 ? m + log(l) : -INFINITY;", "LSE[r] = l > 0.0 ? log(l) : -INFINITY;"),
     "rows_wrong_stride": ("x[j] = widen(X, dtype, (size_t)r * cols + j);", "x[j] = widen(X, dtype, (size_t)r + j);"),
+    "bwd_dropped_scale": ("s[j] = dot * a->scale;", "s[j] = dot;"),
+    "bwd_no_max_shift_in_sum": ("l = l + exp(s[j] - m);", "l = l + exp(s[j]);"),
+    "bwd_drops_D": ("ds = p[j] * (dp - D);", "ds = p[j] * dp;"),
+    "bwd_sign_flip": ("ds = p[j] * (dp - D);", "ds = p[j] * (D - dp);"),
+    "bwd_dk_from_do": ("dK[(size_t)j * d + c] += a->scale * ds * widen(a->Q, a->dtype, qo + c);",
+                       "dK[(size_t)j * d + c] += a->scale * ds * widen(a->dO, a->dtype, qo + c);"),
+    "bwd_dv_uses_ds": ("dV[(size_t)j * d + c] += p[j] * widen(a->dO, a->dtype, qo + c);",
+                       "dV[(size_t)j * d + c] += ds * widen(a->dO, a->dtype, qo + c);"),
+    "bwd_dq_no_scale": ("dQ[(size_t)i * d + c] += a->scale * ds * widen(a->K, a->dtype, ko + c);",
+                        "dQ[(size_t)i * d + c] += ds * widen(a->K, a->dtype, ko + c);"),
+    "bwd_D_drops_output": ("D += widen(a->dO, a->dtype, qo + c) * o[c];", "D += widen(a->dO, a->dtype, qo + c);"),
+    "bwd_dp_reads_k": ("dp += widen(a->dO, a->dtype, qo + c) * widen(a->V, a->dtype, ko + c);",
+                       "dp += widen(a->dO, a->dtype, qo + c) * widen(a->K, a->dtype, ko + c);"),
     "row_index_swapped": ("long bh = flat / a->N, i = flat % a->N, b = bh / a->H;",
                           "long bh = flat / a->N, i = flat % a->N, b = bh % a->B;"),
 }
