@@ -134,6 +134,41 @@ fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t c
     return from_hip(fa::launch_softmax(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_backward_workspace_bytes(int B, int H, int N) {
+    if (B < 0 || H < 0 || N < 0) return 0;
+    return fa::backward_workspace_bytes(B, H, N);
+}
+
+fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                      const float *LSE, void *dQ, void *dK, void *dV, int B, int H, int N, int Nk,
+                      int d, float scale, int causal, const int32_t *key_lens, void *workspace,
+                      size_t workspace_bytes, fa_dtype dtype, void *stream) {
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_BF16 || d != 64) return FA_ERR_UNSUPPORTED;
+    if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0 || (N == 0 && Nk == 0)) return FA_OK;
+    if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if ((long long)(N > Nk ? N : Nk) * d * 2 > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
+    if (N > 0 && (!Q || !O || !dO || !LSE || !dQ)) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!K || !V || !dK || !dV)) return FA_ERR_INVALID_ARG;
+    if (N > 0 && (!aligned16(Q) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
+                  !aligned4(LSE)))
+        return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!aligned16(K) || !aligned16(V) || !aligned16(dK) || !aligned16(dV)))
+        return FA_ERR_INVALID_ARG;
+    if (key_lens && !aligned4(key_lens)) return FA_ERR_INVALID_ARG;
+    const size_t need = fa::backward_workspace_bytes(B, H, N);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+        return FA_ERR_INVALID_ARG;
+    const long long blocks = (long long)B * H * (((N > Nk ? N : Nk) + 127) / 128);
+    if (blocks > kMaxGridX) return FA_ERR_INVALID_ARG;
+    fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, key_lens, B, H, N, Nk, d, scale, causal, workspace};
+    return from_hip(fa::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 void fa_testing_set_softmax_spin_limit(int limit) { fa::set_softmax_spin_limit(limit); }
 
 }  // extern "C"

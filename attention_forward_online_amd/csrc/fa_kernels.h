@@ -37,6 +37,17 @@ struct SoftmaxArgs {
     void *workspace;            // softmax_workspace_bytes(rows, cols, ...) bytes
 };
 
+struct BwdArgs {
+    const void *Q, *K, *V, *O, *dO;
+    const float *LSE;
+    void *dQ, *dK, *dV;
+    const int32_t *key_lens;
+    int B, H, N, Nk, d;
+    float scale;
+    int causal;
+    void *workspace;            // backward_workspace_bytes(B, H, N) bytes
+};
+
 // bf16 prefill, d in {64, 128}: MFMA 32x32x16 bf16 tiles.
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 // fp32 prefill, 1 <= d <= 256: fp32 FMA tiles.
@@ -47,6 +58,9 @@ hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
 // Row softmax / log-sum-exp of a [rows, cols] fp32 or bf16 matrix.
 size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16);
 hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream);
+// bf16 backward, d = 64: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
+size_t backward_workspace_bytes(long long B, long long H, long long N);
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // Test hook: polls of the one-pass wait before its fallback (< 0: default).
 void set_softmax_spin_limit(int limit);
 

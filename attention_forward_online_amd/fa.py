@@ -21,7 +21,8 @@ FA_F32, FA_BF16 = 0, 1
 
 #: every symbol include/fa.h declares
 EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-           "fa_softmax_workspace_bytes", "fa_softmax", "fa_status_str", "fa_last_hip_error")
+           "fa_softmax_workspace_bytes", "fa_softmax", "fa_backward_workspace_bytes", "fa_backward",
+           "fa_status_str", "fa_last_hip_error")
 
 _lib = None
 
@@ -54,6 +55,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_softmax_workspace_bytes.restype = sz
     lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, i, vp, sz, vp]
     lib.fa_softmax.restype = i
+    lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_backward_workspace_bytes.restype = sz
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz,
+                                i, vp]
+    lib.fa_backward.restype = i
     lib.fa_testing_set_softmax_spin_limit.argtypes = [i]
     lib.fa_testing_set_softmax_spin_limit.restype = None
     lib.fa_status_str.argtypes = [i]
@@ -198,6 +204,54 @@ def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
                         ws_bytes, _stream_handle(stream))
     if st != FA_OK:
         raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_backward_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().fa_backward_workspace_bytes(B, H, N))
+
+
+def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=False,
+                key_lens=None, stream=None) -> None:
+    """dQ, dK, dV of sum(dO * O) through the C entry point fa_backward.
+
+    q, o, do, dq: [B,H,N,d]; k, v, dk, dv: [B,H,Nk,d] (bf16); lse: float32
+    [B,H,N] from fa_forward; workspace: a GPU tensor of at least
+    fa_backward_workspace_bytes(B, H, N) bytes.
+    """
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
+                 ("dv", dv)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if (k.shape != (B, H, Nk, d) or v.shape != k.shape or dk.shape != k.shape or dv.shape != k.shape
+            or o.shape != q.shape or do.shape != q.shape or dq.shape != q.shape
+            or lse.shape != (B, H, N)):
+        raise ValueError("shape mismatch between q, k, v, o, do, lse and the gradients")
+    if key_lens is not None:
+        _check_dev("key_lens", key_lens, torch.int32)
+        if key_lens.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                         _ptr(dv), B, H, N, Nk, d, float(scale), int(bool(causal)), _ptr(key_lens),
+                         _ptr(workspace), ws_bytes, _dtype_code(q), _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_backward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, key_lens=None):
+    """Allocate the gradients and the workspace, run fa_backward, return (dQ, dK, dV)."""
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa_backward_workspace_bytes(B, H, N)
+    ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=q.device)
+    fa_backward(q, k, v, o, do, lse, dq, dk, dv, ws, scale=scale, causal=causal, key_lens=key_lens)
+    return dq, dk, dv
 
 
 def testing_set_softmax_spin_limit(limit: int) -> None:

@@ -105,6 +105,8 @@ def main():
                     help="time only the headline prefill (used under the profiler)")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the split-KV decode (used under the profiler)")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the backward on the headline shape (used under the profiler)")
     ap.add_argument("--only-softmax", action="store_true",
                     help="time only the row softmax (used under the profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -146,7 +148,7 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
     # one fa_forward call launches exactly one kernel, so the time per step is
     # that kernel's average launch duration (plus any gap between launches)
-    side_only = args.only_decode or args.only_softmax
+    side_only = args.only_decode or args.only_softmax or args.only_backward
     ms_step = time_region(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
                           args.steps if not side_only else 1,
                           args.warmup if not side_only else 0)
@@ -180,7 +182,7 @@ def main():
 
     if side_only:
         out = {"metric": METRIC}
-    if not args.only_headline and not args.only_softmax:
+    if not args.only_headline and not args.only_softmax and not args.only_backward:
         # ------------------------------------------------------------ decode
         wd = WORKLOADS[DECODE]
         di = make_inputs(wd, device=dev)
@@ -207,7 +209,31 @@ def main():
         del di, od, ld, ws
         torch.cuda.empty_cache()
 
-    if not args.only_headline and not args.only_decode:
+    if not args.only_headline and not args.only_decode and not args.only_softmax:
+        # ------------------------------------------------ backward (headline shape)
+        from attention_forward_online_amd.synth import randn_slices
+        dob = randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nbw = fa.fa_backward_workspace_bytes(w.B, w.H, w.N)
+        wsb = torch.empty(max(nbw, 16) // 4, device=dev, dtype=torch.float32)
+        fa.fa_forward(q, k, v, o, lse, causal=True)
+        ms_b = time_region(lambda: fa.fa_backward(q, k, v, o, dob, lse, dq, dk, dv, wsb, causal=True),
+                           max(5, args.steps // 5), max(2, args.warmup // 2))
+        bflops = 2.5 * flops
+        out["backward"] = {
+            "workload": w.describe() + " backward (dQ, dK, dV from O, dO, LSE)", "name": HEADLINE,
+            "value": round(bflops / (ms_b * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_call": round(ms_b, 5), "flops_per_call": bflops,
+            "flops_convention": "5 GEMMs (QK^T, dP, dV, dK, dQ) = 2.5 x forward, halved for causal",
+            "roofline": {"bound": "mfma", "achieved": round(bflops / (ms_b * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS,
+                         "frac": round(bflops / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "unit": "TFLOP/s", "traffic": None,
+                         "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel"},
+        }
+        del dob, dq, dk, dv, wsb
+
+    if not args.only_headline and not args.only_decode and not args.only_backward:
         # ------------------------------------------------------- row softmax
         wsm = SOFTMAX_WORKLOADS[SOFTMAX]
         xs = make_softmax_input(wsm, device=dev)
@@ -230,7 +256,7 @@ def main():
         del xs, ys, ls, wss
         torch.cuda.empty_cache()
 
-    if not args.only_headline and not args.only_decode and not args.only_softmax:
+    if not (args.only_headline or args.only_decode or args.only_softmax or args.only_backward):
         # ------------------------------------------------- other prefill shapes
         others = {}
         for name in ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",

@@ -149,6 +149,40 @@ size_t fa_softmax_workspace_bytes(int64_t rows, int64_t cols, fa_dtype dtype);
 fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t cols,
                      fa_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Bytes of device workspace fa_backward needs: two fp32 values per query row,
+ * each head's rows padded to a multiple of 64 (8 * B * H * ceil(N / 64) * 64).
+ * Returns 0 for negative arguments.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N);
+
+/*
+ * Attention backward: the gradients of L = sum dO . O with respect to Q, K
+ * and V for O = fa_forward(Q, K, V) with the same scale, causal flag and
+ * key_lens, recomputing the probabilities from the forward's saved LSE
+ * instead of storing them ('Online softmax in attention -- why and how',
+ * "Where this is heading": backward recomputes the scores from the cached
+ * row statistics):
+ *     P_ij = exp(scale q_i . k_j - LSE_i) over the visible keys (0 otherwise),
+ *     D_i = dO_i . O_i,  dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+ *     dV_j = sum_i P_ij dO_i.
+ *   Q, O, dO, dQ: [B, H, N, d]; K, V, dK, dV: [B, H, Nk, d], device, bf16,
+ *   16-byte aligned; LSE: fp32 [B, H, N] as written by fa_forward (-inf for a
+ *   row with no visible key: its dQ row is 0).  Keys no query sees get
+ *   dK = dV = 0.  dQ, dK, dV are written, never accumulated into.
+ *   workspace: device, 16-byte aligned, at least fa_backward_workspace_bytes
+ *   (B, H, N) bytes; contents on entry do not matter.  Calls sharing a
+ *   workspace must not overlap in time.
+ *   Supported: FA_BF16 with d = 64 (fp32 accumulation); anything else gives
+ *   FA_ERR_UNSUPPORTED.  scale finite and > 0.
+ */
+fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                      const float *LSE, void *dQ, void *dK, void *dV,
+                      int B, int H, int N, int Nk, int d, float scale, int causal,
+                      const int32_t *key_lens, void *workspace, size_t workspace_bytes,
+                      fa_dtype dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_str(fa_status status);
 

@@ -187,6 +187,29 @@ def test_softmax_rejects_bad_arguments(lib):
     assert smx(lib, X=None, Y=None, LSE=None, ws=None, rows=0) == fa.FA_OK
 
 
+def test_backward_workspace_and_arguments(lib):
+    assert lib.fa_backward_workspace_bytes(4, 16, 2048) == 8 * 4 * 16 * 2048
+    assert lib.fa_backward_workspace_bytes(1, 2, 77) == 8 * 2 * 128
+    assert lib.fa_backward_workspace_bytes(1, 1, 0) == 0
+    assert lib.fa_backward_workspace_bytes(-1, 1, 5) == 0
+
+    def bwd(Q=P, K=P, V=P, O=P, dO=P, LSE=P, dQ=P, dK=P, dV=P, B=1, H=2, N=100, Nk=100, d=64,
+            scale=0.125, causal=0, key_lens=None, ws=P, ws_bytes=None, dtype=fa.FA_BF16):
+        if ws_bytes is None:
+            ws_bytes = lib.fa_backward_workspace_bytes(B, H, N)
+        return lib.fa_backward(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, Nk, d, scale, causal,
+                               key_lens, ws, ws_bytes, dtype, None)
+    bad, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    assert bwd(dtype=5) == bad and bwd(B=-1) == bad and bwd(causal=2) == bad
+    assert bwd(scale=float("inf")) == bad
+    assert bwd(dtype=fa.FA_F32) == uns and bwd(d=128) == uns and bwd(scale=-1.0) == uns
+    assert bwd(dO=None) == bad and bwd(LSE=None) == bad and bwd(dK=None) == bad
+    assert bwd(dQ=P + 8) == bad and bwd(LSE=P + 2) == bad
+    assert bwd(ws=None) == bad and bwd(ws_bytes=16) == bad
+    assert bwd(B=0, Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None,
+               dV=None, ws=None) == fa.FA_OK
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         fa.load_library(str(tmp_path / "libfa.so"))
