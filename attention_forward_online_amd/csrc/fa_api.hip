@@ -134,6 +134,37 @@ fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t c
     return from_hip(fa::launch_softmax(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_forward_v1_workspace_bytes(int B, int H, int N, int d) {
+    if (B < 0 || H < 0 || N < 0 || d < 0) return 0;
+    return fa::forward_v1_workspace_bytes(B, H, N, d);
+}
+
+fa_status fa_forward_v1(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                        int H, int N, int Nk, int d, float scale, int causal,
+                        const int32_t *key_lens, void *workspace, size_t workspace_bytes,
+                        fa_dtype dtype, void *stream) {
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+    if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * N == 0) return FA_OK;
+    if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
+    if ((long long)(N > Nk ? N : Nk) * d * 4 > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
+    if ((long long)B * H > kMaxGridX) return FA_ERR_INVALID_ARG;
+    if (!Q || !O || !LSE) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE)) return FA_ERR_INVALID_ARG;
+    if (Nk > 0 && (!aligned16(K) || !aligned16(V))) return FA_ERR_INVALID_ARG;
+    if (key_lens && !aligned4(key_lens)) return FA_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) ||
+        workspace_bytes < fa::forward_v1_workspace_bytes(B, H, N, d))
+        return FA_ERR_INVALID_ARG;
+    fa::FwdArgs a{Q, K, V, O, LSE, key_lens, B, H, N, Nk, d, scale, causal};
+    return from_hip(fa::launch_fwd_v1(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_backward_workspace_bytes(int B, int H, int N) {
     if (B < 0 || H < 0 || N < 0) return 0;
     return fa::backward_workspace_bytes(B, H, N);

@@ -58,6 +58,10 @@ hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
 // Row softmax / log-sum-exp of a [rows, cols] fp32 or bf16 matrix.
 size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16);
 hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream);
+// FlashAttention V1 loop order (ablation), bf16, d in {64, 128}; the workspace
+// holds fp32 O, m, l: forward_v1_workspace_bytes(B, H, N, d) bytes.
+size_t forward_v1_workspace_bytes(long long B, long long H, long long N, long long d);
+hipError_t launch_fwd_v1(const FwdArgs &a, void *workspace, hipStream_t stream);
 // bf16 backward, d = 64: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 size_t backward_workspace_bytes(long long B, long long H, long long N);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);

@@ -21,7 +21,8 @@ FA_F32, FA_BF16 = 0, 1
 
 #: every symbol include/fa.h declares
 EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-           "fa_softmax_workspace_bytes", "fa_softmax", "fa_backward_workspace_bytes", "fa_backward",
+           "fa_softmax_workspace_bytes", "fa_softmax", "fa_forward_v1_workspace_bytes",
+           "fa_forward_v1", "fa_backward_workspace_bytes", "fa_backward",
            "fa_status_str", "fa_last_hip_error")
 
 _lib = None
@@ -55,6 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_softmax_workspace_bytes.restype = sz
     lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, i, vp, sz, vp]
     lib.fa_softmax.restype = i
+    lib.fa_forward_v1_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_forward_v1_workspace_bytes.restype = sz
+    lib.fa_forward_v1.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz, i, vp]
+    lib.fa_forward_v1.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, sz,
@@ -204,6 +209,45 @@ def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
                         ws_bytes, _stream_handle(stream))
     if st != FA_OK:
         raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_forward_v1_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_forward_v1_workspace_bytes(B, H, N, d))
+
+
+def fa_forward_v1(q, k, v, o, lse, workspace, scale=None, causal=False, key_lens=None,
+                  stream=None) -> None:
+    """The forward in the V1 loop order (ablation) through fa_forward_v1."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("shape mismatch between q, k, v, o and lse")
+    if key_lens is not None:
+        _check_dev("key_lens", key_lens, torch.int32)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    st = lib.fa_forward_v1(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
+                           float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _dtype_code(q),
+                           _stream_handle(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_forward_v1", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def attention_v1(q, k, v, scale=None, causal=False, key_lens=None):
+    """Allocate O, LSE and the workspace, run fa_forward_v1, return (O, LSE)."""
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = fa_forward_v1_workspace_bytes(B, H, N, d)
+    ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=q.device)
+    fa_forward_v1(q, k, v, o, lse, ws, scale=scale, causal=causal, key_lens=key_lens)
+    return o, lse
 
 
 def fa_backward_workspace_bytes(B: int, H: int, N: int) -> int:

@@ -232,6 +232,21 @@ def main():
                          "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel"},
         }
         del dob, dq, dk, dv, wsb
+        # ------------------------------------ V1 loop order (ablation), headline shape
+        o1 = torch.empty_like(q)
+        l1 = torch.empty_like(lse)
+        nv1 = fa.fa_forward_v1_workspace_bytes(w.B, w.H, w.N, w.d)
+        wv1 = torch.empty(max(nv1, 16) // 4, device=dev, dtype=torch.float32)
+        ms_v1 = time_region(lambda: fa.fa_forward_v1(q, k, v, o1, l1, wv1, causal=True), 5, 1)
+        ms_v2 = time_region(lambda: fa.fa_forward(q, k, v, o1, l1, causal=True), 20, 3)
+        out["v1_ablation"] = {
+            "workload": w.describe() + " in the V1 loop order (KV outer, Q inner, O/m/l via HBM)",
+            "ms_per_call": round(ms_v1, 4), "tflops": round(flops / (ms_v1 * 1e-3) / 1e12, 2),
+            "v2_ms_per_call": round(ms_v2, 5), "v1_over_v2_time": round(ms_v1 / ms_v2, 2),
+            "workspace_bytes": nv1,
+            "note": "one workgroup per (b, h) as in V1: 64 workgroups on 256 CUs",
+        }
+        del o1, l1, wv1
 
     if not args.only_headline and not args.only_decode and not args.only_backward:
         # ------------------------------------------------------- row softmax

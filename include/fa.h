@@ -150,6 +150,30 @@ fa_status fa_softmax(const void *X, void *Y, float *LSE, int64_t rows, int64_t c
                      fa_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace fa_forward_v1 needs: fp32 O, m and l of every
+ * query row, B * H * N * (d + 2) * 4.  Returns 0 for negative arguments.
+ */
+size_t fa_forward_v1_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * The attention forward of fa_forward computed in the FlashAttention V1 loop
+ * order, kept as an ablation ('Online Softmax & FlashAttention' (interview
+ * lesson), Step 2): key/value blocks outside, query blocks inside, one
+ * workgroup per (b, h); for every (key block, query block) pair the
+ * normalised O and the row statistics (m, l) are read from the workspace,
+ * merged with the block (O_new = (l_old e^(m_old - m_new) O_old + P V) / l_new)
+ * and written back.  Same arguments, masking and outputs as fa_forward (O and
+ * LSE agree with it up to rounding), plus the workspace: device, 16-byte
+ * aligned, at least fa_forward_v1_workspace_bytes(B, H, N, d) bytes; its
+ * contents on entry do not matter.
+ *   Supported: FA_BF16 with d in {64, 128}.
+ */
+fa_status fa_forward_v1(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                        int B, int H, int N, int Nk, int d, float scale, int causal,
+                        const int32_t *key_lens, void *workspace, size_t workspace_bytes,
+                        fa_dtype dtype, void *stream);
+
+/*
  * Bytes of device workspace fa_backward needs: two fp32 values per query row,
  * each head's rows padded to a multiple of 64 (8 * B * H * ceil(N / 64) * 64).
  * Returns 0 for negative arguments.
