@@ -178,7 +178,7 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
     if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-    if (dtype != FA_BF16 || d != 64) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
     if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0 || (N == 0 && Nk == 0)) return FA_OK;
     if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;

@@ -1,4 +1,4 @@
-// fa_bwd_bf16.hip -- bf16 attention backward (d = 64) on gfx950 matrix cores.
+// fa_bwd_bf16.hip -- bf16 attention backward (d = 64, 128) on gfx950 matrix cores.
 //
 // The gradients of L = sum dO . O for the forward of fa_fwd_bf16.hip, with the
 // probabilities recomputed from the saved row log-sum-exp instead of being
@@ -279,7 +279,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 }
 
 // dK, dV: 4 waves x 32 keys; Q/dO tiles of 64 queries through two LDS stages.
-template <int D, bool CAUSAL>
+// MODE 0 computes both; at d = 128 both accumulators do not fit next to the
+// operands, so MODE 1 (dV only: S, P, dV) and MODE 2 (dK only: S, dP, dS, dK)
+// run as two launches.
+enum { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
@@ -292,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
     constexpr int KL = kTile * D / 8 / kThreads;
+    constexpr bool WANT_DV = MODE != kOnlyDK, WANT_DK = MODE != kOnlyDV;
     static_assert(kTile * D / 8 % kThreads == 0, "tile/thread mismatch");
 
     __shared__ __attribute__((aligned(16))) uint16_t Qs[NST * TILE];
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         kf[kk] = buffer_load16(ksrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
-        vf[kk] = buffer_load16(vsrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
+        if constexpr (WANT_DK) vf[kk] = buffer_load16(vsrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
     }
     wait_vmem_all();
 
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
             const int i0 = (t_first + t) * kTile;
             f32x16_t s[2], dp[2];
             rows_times(Qs, cur, kf, s);
-            rows_times(Gs, cur, vf, dp);
+            if constexpr (WANT_DK) rows_times(Gs, cur, vf, dp);
             // register v of block qb holds query i0 + 32qb + 16(v/8) + 8g + v%8
             const bool need_mask =
                 !key_vis || (i0 + kTile > N) || (CAUSAL && i0 + off < wk0 + 31);
@@ -446,8 +451,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                         const float d0 = e < 4 ? da[e] : db[e - 4], d1 = e < 4 ? da[e + 1] : db[e - 3];
                         const float p0 = exp2_hw(fmaf(s[qb][v], c, -l0));
                         const float p1 = exp2_hw(fmaf(s[qb][v + 1], c, -l1));
-                        pp[qb][v >> 1] = pack_bf16x2(p0, p1);
-                        pd[qb][v >> 1] = pack_bf16x2(p0 * (dp[qb][v] - d0), p1 * (dp[qb][v + 1] - d1));
+                        if constexpr (WANT_DV) pp[qb][v >> 1] = pack_bf16x2(p0, p1);
+                        if constexpr (WANT_DK)
+                            pd[qb][v >> 1] = pack_bf16x2(p0 * (dp[qb][v] - d0), p1 * (dp[qb][v + 1] - d1));
                     }
                 }
 #pragma unroll
@@ -456,14 +462,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        adv[cb] = mfma32(t_operand(gs_lds, cur, cb, qb, h),
-                                         u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2],
-                                                 pp[qb][4 * h + 3]},
-                                         adv[cb]);
-                        adk[cb] = mfma32(t_operand(qs_lds, cur, cb, qb, h),
-                                         u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2],
-                                                 pd[qb][4 * h + 3]},
-                                         adk[cb]);
+                        if constexpr (WANT_DV)
+                            adv[cb] = mfma32(t_operand(gs_lds, cur, cb, qb, h),
+                                             u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2],
+                                                     pp[qb][4 * h + 3]},
+                                             adv[cb]);
+                        if constexpr (WANT_DK)
+                            adk[cb] = mfma32(t_operand(qs_lds, cur, cb, qb, h),
+                                             u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2],
+                                                     pd[qb][4 * h + 3]},
+                                             adk[cb]);
                     }
         }
         lstore(cur ^ 1);
@@ -485,15 +493,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                     wk[e] = pack_bf16x2(adk[cb][8 * h + 2 * e] * scale, adk[cb][8 * h + 2 * e + 1] * scale);
                     wv[e] = pack_bf16x2(adv[cb][8 * h + 2 * e], adv[cb][8 * h + 2 * e + 1]);
                 }
-                *(u32x4_t *)(krow_out + 32 * cb + 16 * h + 8 * g) = wk;
-                *(u32x4_t *)(vrow_out + 32 * cb + 16 * h + 8 * g) = wv;
+                if constexpr (WANT_DK) *(u32x4_t *)(krow_out + 32 * cb + 16 * h + 8 * g) = wk;
+                if constexpr (WANT_DV) *(u32x4_t *)(vrow_out + 32 * cb + 16 * h + 8 * g) = wv;
             }
     }
 }
 
-template <bool CAUSAL>
-hipError_t launch_bwd64(const BwdArgs &a, hipStream_t stream) {
-    constexpr int D = 64;
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const long long BH = (long long)a.B * a.H;
     const int Npad = (a.N + kTile - 1) / kTile * kTile;
     float *L2 = static_cast<float *>(a.workspace);
@@ -513,10 +520,18 @@ hipError_t launch_bwd64(const BwdArgs &a, hipStream_t stream) {
     }
     if (a.Nk > 0) {
         const int n_kt = (a.Nk + kBk - 1) / kBk;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_kt)), dim3(kThreads), 0,
-                           stream, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
-                           a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, xcd, c, a.scale);
+        auto dkdv = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kt)), dim3(kThreads), 0, stream,
+                               (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                               (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
+                               a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, xcd, c, a.scale);
+        };
+        if constexpr (D == 64) {
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth>);
+        } else {
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV>);
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK>);
+        }
     }
     return hipGetLastError();
 }
@@ -529,7 +544,8 @@ size_t backward_workspace_bytes(long long B, long long H, long long N) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
-    return a.causal ? launch_bwd64<true>(a, stream) : launch_bwd64<false>(a, stream);
+    if (a.d == 64) return a.causal ? launch_bwd<64, true>(a, stream) : launch_bwd<64, false>(a, stream);
+    return a.causal ? launch_bwd<128, true>(a, stream) : launch_bwd<128, false>(a, stream);
 }
 
 }  // namespace fa

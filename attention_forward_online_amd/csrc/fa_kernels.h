@@ -62,7 +62,7 @@ hipError_t launch_softmax(const SoftmaxArgs &a, bool is_bf16, hipStream_t stream
 // holds fp32 O, m, l: forward_v1_workspace_bytes(B, H, N, d) bytes.
 size_t forward_v1_workspace_bytes(long long B, long long H, long long N, long long d);
 hipError_t launch_fwd_v1(const FwdArgs &a, void *workspace, hipStream_t stream);
-// bf16 backward, d = 64: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
+// bf16 backward, d in {64, 128}: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 size_t backward_workspace_bytes(long long B, long long H, long long N);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // Test hook: polls of the one-pass wait before its fallback (< 0: default).

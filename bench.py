@@ -228,7 +228,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(bflops / (ms_b * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS,
                          "frac": round(bflops / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "unit": "TFLOP/s", "traffic": None,
+                         "unit": "TFLOP/s", "traffic": measured_traffic("backward/" + HEADLINE),
                          "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel"},
         }
         del dob, dq, dk, dv, wsb
@@ -297,6 +297,18 @@ def main():
             else:
                 rec["frac"] = round(nominal / (ms_o * 1e-3) / 1e12 / peak, 4)
             rec["peak"] = peak
+            if name == "causal_bf16_b1h32_n8192_d128":
+                # backward of the same shape (5-GEMM convention, 2.5 x forward FLOPs)
+                from attention_forward_online_amd.synth import randn_slices
+                dg = randn_slices(tuple(oi["q"].shape), 1.0, torch.bfloat16, 0, wo.name, "do", dev)
+                gq, gk, gv = (torch.empty_like(oi[t]) for t in ("q", "k", "v"))
+                wsz = fa.fa_backward_workspace_bytes(wo.B, wo.H, wo.N)
+                wsg = torch.empty(max(wsz, 16) // 4, device=dev, dtype=torch.float32)
+                ms_g = time_region(lambda: fa.fa_backward(oi["q"], oi["k"], oi["v"], oo, dg, ol, gq, gk, gv,
+                                                          wsg, causal=True), 3, 1)
+                rec["backward_ms_per_call"] = round(ms_g, 4)
+                rec["backward_tflops"] = round(2.5 * nominal / (ms_g * 1e-3) / 1e12, 2)
+                del dg, gq, gk, gv, wsg
             others[name] = rec
             del oi, oo, ol
         out["workloads"] = others

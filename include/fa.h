@@ -198,8 +198,8 @@ size_t fa_backward_workspace_bytes(int B, int H, int N);
  *   workspace: device, 16-byte aligned, at least fa_backward_workspace_bytes
  *   (B, H, N) bytes; contents on entry do not matter.  Calls sharing a
  *   workspace must not overlap in time.
- *   Supported: FA_BF16 with d = 64 (fp32 accumulation); anything else gives
- *   FA_ERR_UNSUPPORTED.  scale finite and > 0.
+ *   Supported: FA_BF16 with d in {64, 128} (fp32 accumulation); anything else
+ *   gives FA_ERR_UNSUPPORTED.  scale finite and > 0.
  */
 fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV,

@@ -1,4 +1,4 @@
-"""GPU parity of the bf16 attention backward (fa_backward, d = 64) against the
+"""GPU parity of the bf16 attention backward (fa_backward, d = 64 and 128) against the
 fp64 oracle's exact gradients on the same stored inputs.
 
 The GPU path starts from its own forward (bf16 O, fp32 LSE), rounds P and dS to
@@ -26,9 +26,9 @@ DEV = "cuda:0"
 REL, ABS = 2e-2, 1e-3
 
 
-def make(B, H, N, Nk, seed, key_lens=None):
-    inp = synth.random_case(B, H, N, Nk, 64, torch.bfloat16, seed=seed, device=DEV, key_lens=key_lens)
-    do = synth.randn_slices((B, H, N, 64), 1.0, torch.bfloat16, seed, f"bwd_{B}_{H}_{N}_{Nk}", "do", DEV)
+def make(B, H, N, Nk, seed, key_lens=None, d=64):
+    inp = synth.random_case(B, H, N, Nk, d, torch.bfloat16, seed=seed, device=DEV, key_lens=key_lens)
+    do = synth.randn_slices((B, H, N, d), 1.0, torch.bfloat16, seed, f"bwd_{B}_{H}_{N}_{Nk}_{d}", "do", DEV)
     return inp["q"], inp["k"], inp["v"], do, inp["key_lens"]
 
 
@@ -87,6 +87,19 @@ def test_shapes(N, Nk, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,Nk", [(128, 128), (77, 130), (130, 77), (300, 300)])
+def test_shapes_d128(N, Nk, causal):
+    q, k, v, do, kl = make(1, 2, N, Nk, seed=N * 1000 + Nk + 1, d=128)
+    run_and_check(q, k, v, do, kl, causal, what=f"d128 shapes {N}x{Nk}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_lens_d128(causal):
+    q, k, v, do, kl = make(2, 2, 150, 190, seed=17, key_lens=[101, 0], d=128)
+    run_and_check(q, k, v, do, kl, causal, what="d128 key_lens")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_key_lens_and_empty_batch(causal):
     q, k, v, do, kl = make(2, 2, 150, 190, seed=7, key_lens=[101, 0])
     run_and_check(q, k, v, do, kl, causal, what="key_lens")
@@ -128,3 +141,11 @@ def test_full_size_headline_shape():
     inp = synth.make_inputs(w, device=DEV)
     do = synth.randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", DEV)
     run_and_check(inp["q"], inp["k"], inp["v"], do, None, True, heads=[0, 45], what="headline shape")
+
+
+def test_full_size_long_d128_shape():
+    # B1 H32 N=Nk=8192 d128 causal (the long prefill shape); one head in full
+    w = synth.WORKLOADS["causal_bf16_b1h32_n8192_d128"]
+    inp = synth.make_inputs(w, device=DEV)
+    do = synth.randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", DEV)
+    run_and_check(inp["q"], inp["k"], inp["v"], do, None, True, heads=[21], what="8192-long d128")
