@@ -178,11 +178,13 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
     if (B < 0 || H < 0 || N < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-    if (dtype != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_F32 && d > 128) return FA_ERR_UNSUPPORTED;
     if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0 || (N == 0 && Nk == 0)) return FA_OK;
     if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
-    if ((long long)(N > Nk ? N : Nk) * d * 2 > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
+    if ((long long)(N > Nk ? N : Nk) * d * (dtype == FA_BF16 ? 2 : 4) > kMaxSliceBytes)
+        return FA_ERR_INVALID_ARG;
     if (N > 0 && (!Q || !O || !dO || !LSE || !dQ)) return FA_ERR_INVALID_ARG;
     if (Nk > 0 && (!K || !V || !dK || !dV)) return FA_ERR_INVALID_ARG;
     if (N > 0 && (!aligned16(Q) || !aligned16(O) || !aligned16(dO) || !aligned16(dQ) ||
@@ -194,10 +196,11 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
     const size_t need = fa::backward_workspace_bytes(B, H, N);
     if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
         return FA_ERR_INVALID_ARG;
-    const long long blocks = (long long)B * H * (((N > Nk ? N : Nk) + 127) / 128);
+    const long long blocks = (long long)B * H * (((N > Nk ? N : Nk) + 63) / 64);
     if (blocks > kMaxGridX) return FA_ERR_INVALID_ARG;
     fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, key_lens, B, H, N, Nk, d, scale, causal, workspace};
-    return from_hip(fa::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 
 void fa_testing_set_softmax_spin_limit(int limit) { fa::set_softmax_spin_limit(limit); }

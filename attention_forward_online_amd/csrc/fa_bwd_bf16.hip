@@ -37,15 +37,6 @@ constexpr int kBk = 128;     // keys per dK/dV workgroup (32 per wave)
 constexpr int kTile = 64;    // keys per K/V tile (dQ) and queries per Q/dO tile (dK/dV)
 constexpr int kPad = 8;      // bf16 pad per LDS row
 
-__device__ __forceinline__ int perm32(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Workgroup -> (head, block rank); with B*H divisible by 8 all blocks of a
 // head run on one XCD (round-robin dispatch), as in the forward.
 __device__ __forceinline__ void block_of(int bid, int nblk, int xcd_interleave, int &bh, int &rank) {

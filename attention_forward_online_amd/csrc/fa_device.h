@@ -77,6 +77,23 @@ __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Row order of a 32-row MFMA operand block: operand row r reads row perm32(r)
+// (bits 2 and 3 swapped).  With it the 32x32 accumulator registers 8h..8h+7
+// of lane half g hold rows 16h + 8g + 0..7 -- eight consecutive rows, which is
+// the k-layout of the next MFMA's operand, so scores feed P.V (and P, dS feed
+// the backward products) without any register shuffle.
+__device__ __forceinline__ int perm32(int r) {
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// D = A B + C on v_mfma_f32_32x32x16_bf16: A row / B column = lane % 32, the
+// 8 k values of each lane at k offset 8 * (lane / 32); D column = lane % 32,
+// rows 8(v/4) + 4(lane/32) + v%4 in register v.
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Even split of a clamped key length: the visible keys of batch b.
 __device__ __forceinline__ int visible_len(const int32_t *key_lens, int b, int Nk) {
     if (!key_lens) return Nk;

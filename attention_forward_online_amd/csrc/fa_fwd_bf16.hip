@@ -64,16 +64,6 @@ constexpr int kBc = 64;                     // keys per K/V tile
 constexpr int kPad = 8;                     // bf16 pad per K/V row in LDS
 constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
 
-// Operand row r of a 32-row MFMA block reads key (or V column) perm32(r).
-__device__ __forceinline__ int perm32(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(

@@ -26,15 +26,6 @@ constexpr int kBr = 128;     // query rows per inner block (32 per wave)
 constexpr int kBc = 64;      // keys per outer block
 constexpr int kPad = 8;
 
-__device__ __forceinline__ int perm32(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_v1_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,

@@ -65,6 +65,8 @@ hipError_t launch_fwd_v1(const FwdArgs &a, void *workspace, hipStream_t stream);
 // bf16 backward, d in {64, 128}: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 size_t backward_workspace_bytes(long long B, long long H, long long N);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+// fp32 backward, 1 <= d <= 128 (same workspace layout).
+hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t stream);
 // Test hook: polls of the one-pass wait before its fallback (< 0: default).
 void set_softmax_spin_limit(int limit);
 

@@ -191,15 +191,16 @@ size_t fa_backward_workspace_bytes(int B, int H, int N);
  *     D_i = dO_i . O_i,  dS_ij = P_ij (dO_i . v_j - D_i),
  *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
  *     dV_j = sum_i P_ij dO_i.
- *   Q, O, dO, dQ: [B, H, N, d]; K, V, dK, dV: [B, H, Nk, d], device, bf16,
- *   16-byte aligned; LSE: fp32 [B, H, N] as written by fa_forward (-inf for a
+ *   Q, O, dO, dQ: [B, H, N, d]; K, V, dK, dV: [B, H, Nk, d], device, element
+ *   type `dtype`, 16-byte aligned; LSE: fp32 [B, H, N] as written by fa_forward (-inf for a
  *   row with no visible key: its dQ row is 0).  Keys no query sees get
  *   dK = dV = 0.  dQ, dK, dV are written, never accumulated into.
  *   workspace: device, 16-byte aligned, at least fa_backward_workspace_bytes
  *   (B, H, N) bytes; contents on entry do not matter.  Calls sharing a
  *   workspace must not overlap in time.
- *   Supported: FA_BF16 with d in {64, 128} (fp32 accumulation); anything else
- *   gives FA_ERR_UNSUPPORTED.  scale finite and > 0.
+ *   Supported: FA_BF16 with d in {64, 128} (bf16 MFMA operands, fp32
+ *   accumulation) and FA_F32 with 1 <= d <= 128 (fp32 throughout); anything
+ *   else gives FA_ERR_UNSUPPORTED.  scale finite and > 0.
  */
 fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV,
