@@ -48,6 +48,23 @@ __device__ __forceinline__ u32x4_t buffer_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// 16-byte buffer load straight into LDS (no register stage): lane l of the
+// wave writes bytes lds + 16 l .. lds + 16 l + 15; a lane whose offset fails the
+// range check writes zeros, an inactive lane writes nothing.  `lds` is
+// wave-uniform (it goes to M0).  The write is tracked by the vector-memory
+// counter: wait_vmem_all() and a barrier before other waves read it.
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, void *lds, uint32_t byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             byte_off, 0, 0, 0);
+}
+
+// Keep a value computed at this point of the instruction stream: an empty
+// volatile asm reads and redefines the register, so the computation cannot
+// be sunk past it towards its first use (used to interleave VALU work with
+// matrix instructions that the scheduler would otherwise separate).
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane s supplies the LDS address of 4 consecutive 16-bit elements (a row
 // chunk); lane L receives element L % 4 of the chunks of lanes L/4 + 4t,

@@ -35,21 +35,23 @@
 //     by more than 2^8 (FA-4's thresholded rescale); o and l always share the
 //     reference, so the result is unchanged while most tiles skip the
 //     rescale of the accumulators.
+//   * Software pipeline within each wave: iteration t issues the MFMAs of
+//     S(t+1) = K(t+1) Q^T with the exponentials of tile t between them, then
+//     the MFMAs of O += P(t) V(t) with the rest of those exponentials and the
+//     row max of tile t+1 between them, so the matrix pipe and the vector ALUs
+//     of one wave work at the same time.  Scheduling barriers fix the order of
+//     each MFMA and its VALU group; pin() keeps the compiler from sinking the
+//     VALU work towards its later uses.  The loop is unrolled by two so that
+//     S(t) and S(t+1) alternate between two register sets without copies.
+//   * K/V tiles go from HBM straight into LDS (buffer loads with the LDS flag,
+//     no register stage), which keeps d = 64 within three waves per SIMD and
+//     d = 128 without spills.  K runs two tiles ahead, V one: iteration t
+//     loads K(t+2) into the stage K(t) left and V(t+1) into the stage V(t-1)
+//     left, and they land before the iteration's only barrier.
 //   * Work order: one query block per workgroup, causal launches start with
 //     the longest blocks; all blocks of a head run on one XCD (the dispatcher
 //     deals workgroup ids to the 8 XCDs round-robin), so K/V re-reads of a
-//     head hit one L2, and consecutive heads go to different XCDs.  (Pairing
-//     blocks n-1-u and u in one workgroup evens the work but halves the
-//     waves per SIMD; it measured slower.)
-//   * The MFMA sections run at raised wave priority (s_setprio 1), so the
-//     arbiter issues a waiting wave's MFMAs ahead of the other wave's VALU
-//     work and the matrix pipe stays fed.
-//   * Two LDS stages, one barrier per tile: tile t is computed from one stage
-//     while the other receives tile t+1 from registers; the global loads of
-//     tile t+2 are in flight meanwhile.  Tiles are processed in order, with
-//     the two waves of each SIMD (two workgroups per CU) overlapping one
-//     wave's softmax with the other's MFMAs.  (Software-pipelining the next
-//     tile's QK^T into the softmax within a wave measured slower on gfx950.)
+//     head hit one L2, and consecutive heads go to different XCDs.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -63,6 +65,9 @@ constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                     // keys per K/V tile
 constexpr int kPad = 8;                     // bf16 pad per K/V row in LDS
 constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
+constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
+
+template <int N_> struct IntC { static constexpr int value = N_; };
 
 // d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.
 template <int D, bool CAUSAL>
@@ -71,28 +76,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
     float c) {
-    constexpr int NST = 2;                      // LDS stages
     constexpr int KS = D + kPad;                // K and V row stride in LDS (elements)
     constexpr int TILE = kBc * KS;              // elements per stage of K (or V)
     constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
     constexpr int CB = D / 32;                  // 32-column blocks of O^T
-    constexpr int KCH = kBc * D / 8;            // 16-byte chunks per K (or V) tile
-    constexpr int KL = KCH / kThreads;          // ... per thread
-    static_assert(KCH % kThreads == 0, "tile/thread mismatch");
+    constexpr int NS = 2 * KK;                  // S MFMAs per tile (= P pairs made beside them)
+    constexpr int NP2 = 4 * CB;                 // P.V MFMAs per tile
+    constexpr int PAIRS2 = 16 - NS;             // P pairs left for the P.V section
+    constexpr int PD = kPrefetch;
+    static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[NST * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[NST * TILE];
+    // one array per stage, so that the stage a load fills and the stage the
+    // MFMAs read are distinct objects
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE], Vs1[TILE];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < kWaves);
     const int li = lane & 31, g = lane >> 5;
     const int krow = perm32(li);
-    // V^T operand through the transpose read: lane (li, g) reads the 4-element
-    // chunk at key row vrow (+ the block's first key) and column vcol; lane li
-    // then receives V column perm32(li) of 4 consecutive keys
     const int vrow = (li & 15) >> 2;
     const int vcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    const __attribute__((address_space(3))) uint16_t *vs_lds =
-        (const __attribute__((address_space(3))) uint16_t *)&Vs[0];
+    auto kst = [&](int stage) -> uint16_t * { return stage ? Ks1 : Ks0; };
+    auto vst = [&](int stage) -> uint16_t * { return stage ? Vs1 : Vs0; };
 
     // workgroup -> (head, query block).  With B*H divisible by 8, head bh lives on
     // XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs round-robin):
@@ -110,206 +117,240 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     }
     const int b = bh / H;
     const int off = Nk - N;                     // causal: key j visible to query i iff j <= i + off
-    const int kv_lim = visible_len(key_lens, b, Nk);
+    const int kv_lim = __builtin_amdgcn_readfirstlane(visible_len(key_lens, b, Nk));
     const size_t q_base = (size_t)bh * N * D;
     const size_t kv_base = (size_t)bh * Nk * D;
-    const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);   // rows >= N read as 0
+    const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);
 
-    // One query block per workgroup; causal launches hand out the longest
-    // blocks (the last ones) first.
-    {
-        const int qtile = CAUSAL ? n_qtiles - 1 - rank : rank;
-        const int q0 = qtile * kBr;
-        int kv_end = kv_lim;
-        if (CAUSAL) kv_end = min(kv_end, min(q0 + kBr, N) - 1 + off + 1);
-        const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
-        const int wq_first = q0 + wave * kRowsPerWave;
-        const int wq_last = min(wq_first + kRowsPerWave, N) - 1;   // < wq_first: no rows
-        const int qrow = wq_first + li;
-        const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)kv_end * D * 2);   // rows >= kv_end read as 0
-        const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)kv_end * D * 2);
+    // causal launches hand out the longest blocks (the last ones) first
+    const int qtile = CAUSAL ? n_qtiles - 1 - rank : rank;
+    const int q0 = qtile * kBr;
+    int kv_end = kv_lim;
+    if (CAUSAL) kv_end = min(kv_end, min(q0 + kBr, N) - 1 + off + 1);
+    const int ntiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
+    const int wq_first = q0 + wave * kRowsPerWave;
+    const int wq_last = min(wq_first + kRowsPerWave, N) - 1;
+    const int qrow = wq_first + li;
+    // tiles this wave sees: a prefix of the workgroup's tiles
+    int nt_w = 0;
+    if (wq_first <= wq_last) {
+        const int last_key = wq_last + off;
+        nt_w = !CAUSAL ? ntiles : (last_key < 0 ? 0 : min(ntiles, last_key / kBc + 1));
+    }
 
-        u32x4_t qf[KK];
+    u32x4_t qf[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qf[kk] = buffer_load16(qsrc, (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2);
-        // settle Q before the loop so that no wait inside it covers the prefetch
-        wait_vmem_all();
+    for (int kk = 0; kk < KK; ++kk)
+        qf[kk] = buffer_load16(qsrc, (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2);   // rows >= N read 0
+    wait_vmem_all();
 
-        f32x16_t acc[CB];
+    f32x16_t acc[CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
-        // Reference max in log2 units (scale*log2(e)*score).  It moves only when
-        // a tile's max exceeds it by more than kLazyTau (thresholded lazy
-        // rescale, 'Online Softmax' research-hub page, "Why it matters"): the
-        // weights 2^(s - ref) then stay below 2^kLazyTau, and o and l always
-        // share one reference, so o / l and ref + log2 l are exact.
-        float ms = neg_inf();
-        float l = 0.f;          // this lane's half of the running denominator
+        for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
+    // Reference max in log2 units (scale*log2(e)*score).  It moves only when
+    // a tile's max exceeds it by more than kLazyTau (thresholded lazy
+    // rescale, 'Online Softmax' research-hub page, "Why it matters"): the
+    // weights 2^(s - ref) then stay below 2^kLazyTau, and o and l always
+    // share one reference, so o / l and ref + log2 l are exact.
+    float ms = neg_inf();
+    float ref = 0.f;        // the reference the next probabilities use (0 while ms = -inf)
+    float l = 0.f;          // this lane's half of the running denominator
 
-        // Register stage for the global -> LDS copy.  Loads past the last tile
-        // fall outside the buffer range and return zeros without touching
-        // memory, so they are issued unconditionally (straight-line code keeps
-        // the vmcnt waits partial).
-        u32x4_t kr[KL], vr[KL];
-        auto gload = [&](int t, u32x4_t (&kr)[KL], u32x4_t (&vr)[KL]) {
-            const int j0 = t * kBc;
+    // K/V tiles go from HBM straight into LDS (16-byte buffer loads with the
+    // LDS flag: lane l of a wave's load fills bytes 16 l .. 16 l + 15 of a 1 KiB
+    // window).  A stage of KS-element rows is NJ such windows; wave w issues
+    // windows w, w + 4, ...  Each lane's global offset within the tile is fixed:
+    // its window position's row and 16-byte column, or an offset past every
+    // buffer for the row padding (the range check then writes zeros).
+    constexpr int RB = KS * 2;                  // LDS row bytes
+    constexpr int NJ = kBc * RB / 1024;         // 1 KiB windows per stage
+    constexpr int MJ = (NJ + kWaves - 1) / kWaves;
+    static_assert(NJ * 1024 == kBc * RB, "stage is not a whole number of windows");
+    uint32_t goff[MJ];
 #pragma unroll
-            for (int p = 0; p < KL; ++p) {
-                const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-                const uint32_t off_b = (uint32_t)((j0 + row) * D + 8 * col8) * 2;
-                kr[p] = buffer_load16(ksrc, off_b);
-                vr[p] = buffer_load16(vsrc, off_b);
-            }
-        };
-        auto lstore = [&](int stage, const u32x4_t (&kr)[KL], const u32x4_t (&vr)[KL]) {
+    for (int m = 0; m < MJ; ++m) {
+        const int p = 1024 * (wave + kWaves * m) + 16 * lane;
+        const int r = p / RB, q = (p % RB) / 16;
+        goff[m] = (q < D / 8 && r < kBc) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
+    }
+    auto dma = [&](const uint16_t *src, uint16_t *dst, int t) {
+        const int j0 = t * kBc;
+        const rsrc_t r = make_rsrc(src + (size_t)j0 * D, (uint32_t)max(kv_end - j0, 0) * D * 2);
 #pragma unroll
-            for (int p = 0; p < KL; ++p) {
-                const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-                *(u32x4_t *)&Ks[stage * TILE + row * KS + 8 * col8] = kr[p];
-                *(u32x4_t *)&Vs[stage * TILE + row * KS + 8 * col8] = vr[p];
-            }
-        };
-        auto active = [&](int t) {   // wave-uniform; a prefix of the tiles
-            return wq_first <= wq_last && (!CAUSAL || t * kBc <= wq_last + off);
-        };
-        // S^T of one 64-key tile (two 32-key blocks) x this wave's 32 queries,
-        // operands read from LDS as the MFMAs need them
-        auto qk_lds = [&](int stage, f32x16_t (&s)[2]) {
+        for (int m = 0; m < MJ; ++m)
+            if (wave + kWaves * m < NJ)
+                buffer_load_lds16(r, (char *)dst + 1024 * (wave + kWaves * m), goff[m]);
+    };
+    const uint16_t *kg = K + kv_base, *vg = V + kv_base;
+    // operand of S MFMA i (block jb = i % 2, k-step kk = i / 2) from the K tile in `stage`
+    auto k_operand = [&](int stage, int i) {
+        const int jb = i & 1, kk = i >> 1;
+        return *(const u32x4_t *)&kst(stage)[(32 * jb + krow) * KS + 8 * g + 16 * kk];
+    };
+    // operand of P.V MFMA i (chunk ci = i / CB = 2 jb + h, column block cb = i % CB)
+    auto v_operand = [&](int stage, int i) {
+        const int ci = i / CB, cb = i % CB, jb = ci >> 1, h = ci & 1;
+        const auto *p0 = (const __attribute__((address_space(3))) uint16_t *)vst(stage) +
+                         (8 * g + vrow + 32 * jb + 16 * h) * KS + vcol + 32 * cb;
+        const u32x2_t lo = lds_read_tr16(p0);
+        const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // P pair q (chunk q / 4, scores 2(q % 4), +1 of it): 2^(s c - ref) in fp32 into the
+    // row sum, bf16 pair into the MFMA operand
+    auto p_pair = [&](const f32x16_t (&s)[2], int q, uint32_t (&pk)[4][4], float (&rs)[4]) {
+        const int ci = q >> 2, e = q & 3, jb = ci >> 1, v = 8 * (ci & 1) + 2 * e;
+        const float p0 = exp2_hw(fmaf(s[jb][v], c, -ref));
+        const float p1 = exp2_hw(fmaf(s[jb][v + 1], c, -ref));
+        rs[q & 3] += p0 + p1;
+        pk[ci][e] = pack_bf16x2(p0, p1);
+        pin(rs[q & 3]);
+        pin(pk[ci][e]);
+    };
+    auto max8 = [&](const f32x16_t (&s)[2], int k) {
+        const f32x16_t &x = s[k >> 1];
+        const int v0 = 8 * (k & 1);
+        return fmaxf(fmaxf(fmaxf(x[v0], x[v0 + 1]), x[v0 + 2]),
+                     fmaxf(fmaxf(x[v0 + 3], x[v0 + 4]), fmaxf(fmaxf(x[v0 + 5], x[v0 + 6]), x[v0 + 7])));
+    };
+    auto need_mask = [&](int t) {
+        const int j0 = t * kBc;
+        return (j0 + kBc > kv_lim) || (CAUSAL && j0 + kBc - 1 > wq_first + off);
+    };
+    auto apply_mask = [&](int t, f32x16_t (&sc)[2]) {
+        const int j0 = t * kBc;
+        const int vis_end = CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim;
+        const int lim = vis_end - j0 - 8 * g;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                const uint16_t *kp = &Ks[stage * TILE + (32 * jb + krow) * KS + 8 * g];
-                s[jb] = mfma32(*(const u32x4_t *)kp, qf[0], f32x16_t{});
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-                for (int kk = 1; kk < KK; ++kk)
-                    s[jb] = mfma32(*(const u32x4_t *)(kp + 16 * kk), qf[kk], s[jb]);
-            }
-        };
-        // V^T operand (A of the P.V MFMA) for keys 32jb + 16h + 8g + 0..7 and
-        // V column 32cb + perm32(li) of the tile in `stage`
-        auto v_operand = [&](int stage, int cb, int jb, int h) {
-            const auto *p0 =
-                vs_lds + stage * TILE + (8 * g + vrow + 32 * jb + 16 * h) * KS + vcol + 32 * cb;
-            const u32x2_t lo = lds_read_tr16(p0);
-            const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
-            return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        };
-        // masking, row max and the (rare) move of the reference; returns the
-        // reference the probabilities of this tile use
-        auto softmax_prep = [&](int t, f32x16_t (&sc)[2]) {
-            const int j0 = t * kBc;
-            const bool need_mask =
-                (j0 + kBc > kv_lim) || (CAUSAL && j0 + kBc - 1 > wq_first + off);
-            if (need_mask) {
-                // register v of block jb holds key j0 + 32jb + 16(v/8) + 8g + v%8;
-                // keys at or past this lane's limit are invisible
-                const int vis_end = CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim;
-                const int lim = vis_end - j0 - 8 * g;
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) sc[jb][v] = neg_inf();
-            }
-            // tile row max: four independent chains over the 32 in-lane keys,
-            // the other 32 keys in lane ^ 32
-            float m4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x16_t &s = sc[i >> 1];
-                const int v0 = 8 * (i & 1);
-                m4[i] = fmaxf(fmaxf(fmaxf(s[v0], s[v0 + 1]), s[v0 + 2]),
-                              fmaxf(fmaxf(s[v0 + 3], s[v0 + 4]),
-                                    fmaxf(fmaxf(s[v0 + 5], s[v0 + 6]), s[v0 + 7])));
-            }
-            const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
-            // move the reference only when this row's max got too far ahead
-            const bool move = mx > ms + kLazyTau;   // false for a fully masked tile
-            if (__any(move)) {
-                // lanes that keep their reference use alpha = 1 (never
-                // exp2(ms - ms), which is NaN while ms is still -inf)
-                const float alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
-                l *= alpha;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
-                ms = move ? mx : ms;
-            }
-            return ms == neg_inf() ? 0.f : ms;   // -inf guard: all P = 0 then
-        };
-        // P = 2^(s c - ref) for this lane's 32 scores: bf16 pairs for the MFMA,
-        // fp32 values into the row sum (four partial sums)
-        auto probabilities = [&](const f32x16_t (&sc)[2], float ms_ref, uint32_t (&pk)[2][8]) {
-            float r4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const float p0 = exp2_hw(fmaf(sc[jb][v], c, -ms_ref));
-                    const float p1 = exp2_hw(fmaf(sc[jb][v + 1], c, -ms_ref));
-                    r4[(v >> 1) & 3] += p0 + p1;
-                    pk[jb][v >> 1] = pack_bf16x2(p0, p1);
-                }
-            return (r4[0] + r4[1]) + (r4[2] + r4[3]);
-        };
-        auto p_operand = [&](const uint32_t (&pk)[2][8], int jb, int h) {
-            return u32x4_t{pk[jb][4 * h], pk[jb][4 * h + 1], pk[jb][4 * h + 2], pk[jb][4 * h + 3]};
-        };
-
-        // tiles in order from two LDS stages; the loads of tile t+1 are in
-        // flight while tile t is computed
-        gload(0, kr, vr);
-        lstore(0, kr, vr);
-        gload(1, kr, vr);
-        __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int cur = t & 1;
-            if (active(t)) {
-                f32x16_t sc[2];
-                __builtin_amdgcn_s_setprio(1);
-                qk_lds(cur, sc);
-                __builtin_amdgcn_s_setprio(0);
-                const float ms_ref = softmax_prep(t, sc);
-                uint32_t pk[2][8];
-                l += probabilities(sc, ms_ref, pk);
-                __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            acc[cb] = mfma32(v_operand(cur, cb, jb, h), p_operand(pk, jb, h),
-                                             acc[cb]);
-                __builtin_amdgcn_s_setprio(0);
-            }
-            lstore(cur ^ 1, kr, vr);    // tile t+1
-            gload(t + 2, kr, vr);
-            __syncthreads();
-        }
-
-        // epilogue: O = o / l (0 for a row without keys), LSE = ref + log2 l in nats (-inf then)
-        const float lt = l + shfl_xor_f32(l, 32);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        if (qrow < N) {
-            uint16_t *orow = O + q_base + (size_t)qrow * D;
+            for (int v = 0; v < 16; ++v)
+                if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) sc[jb][v] = neg_inf();
+    };
+    // lazy move of the reference after a tile's row max mx (log2 units)
+    auto decide = [&](float mx) {
+        const bool move = mx > ms + kLazyTau;   // false for a fully masked tile
+        if (__any(move)) {
+            const float alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
+            l *= alpha;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4_t w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = pack_bf16x2(acc[cb][8 * h + 2 * e] * inv,
-                                           acc[cb][8 * h + 2 * e + 1] * inv);
-                    *(u32x4_t *)(orow + 32 * cb + 16 * h + 8 * g) = w;
-                }
-            if (g == 0)
-                LSE[(size_t)bh * N + qrow] = lt > 0.f ? (ms + log2_hw(lt)) * kLn2 : neg_inf();
+                for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
+            ms = move ? mx : ms;
         }
+        ref = ms == neg_inf() ? 0.f : ms;
+    };
+    auto rowmax = [&](const float (&m4)[4]) {
+        return max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+    };
+
+    // prologue: K(0), V(0), K(1) into LDS, then S(0) prepared
+    dma(kg, Ks0, 0);
+    dma(vg, Vs0, 0);
+    dma(kg, Ks1, 1);
+    wait_vmem_all();
+    __syncthreads();
+    f32x16_t sa[2], sb[2];
+    if (nt_w > 0) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            sa[i & 1] = mfma32(k_operand(0, i), qf[i >> 1], i < 2 ? f32x16_t{} : sa[i & 1]);
+        if (need_mask(0)) apply_mask(0, sa);
+        float m4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m4[k] = max8(sa, k);
+        decide(rowmax(m4));
+    }
+    __syncthreads();
+
+    // iteration t: K(t+2) and V(t+1) are loaded into the stages K(t) and
+    // V(t-1) left; S(t+1) is computed from K(t+1) beside the exponentials of
+    // tile t, then O += P(t) V(t) beside the rest of them and the row max of
+    // tile t+1.  One barrier per iteration.  On a wave's last tile the S(t+1)
+    // products are computed but not used (the stage then holds zeros or
+    // another wave's next tile).
+    auto refill = [&](int par, int t) {   // K(t+2), V(t+1); they land before the barrier
+        dma(kg, kst(par), t + 2);
+        dma(vg, vst(par ^ 1), t + 1);
+    };
+    auto step = [&](auto par_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+        constexpr int par = decltype(par_c)::value;
+        refill(par, t);
+        uint32_t pk[4][4];
+        float rs[4] = {-0.f, -0.f, -0.f, -0.f};
+        u32x4_t kop[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) kop[i] = k_operand(par ^ 1, i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
+            if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
+            p_pair(sc, i, pk, rs);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const bool more = t + 1 < nt_w;
+        if (more && need_mask(t + 1)) apply_mask(t + 1, sn);
+        float m4[4];
+        u32x4_t vop[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) vop[i] = v_operand(par, i);
+#pragma unroll
+        for (int i = 0; i < NP2; ++i) {
+            const int ci = i / CB;
+            acc[i % CB] = mfma32(vop[i % PD], u32x4_t{pk[ci][0], pk[ci][1], pk[ci][2], pk[ci][3]},
+                                 acc[i % CB]);
+            if (i + PD < NP2) vop[i % PD] = v_operand(par, i + PD);
+            if (i < PAIRS2 / 2) {
+                p_pair(sc, NS + 2 * i, pk, rs);
+                p_pair(sc, NS + 2 * i + 1, pk, rs);
+            }
+            if (i >= NP2 - 4) {
+                m4[i - (NP2 - 4)] = max8(sn, i - (NP2 - 4));
+                pin(m4[i - (NP2 - 4)]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        if (more) decide(rowmax(m4));
+        wait_vmem_all();
+        __syncthreads();
+    };
+    // every wave passes ntiles barriers: nt_w in its own tiles, the rest in the
+    // refill-only loop
+    int t = 0;
+    for (; t + 2 <= nt_w; t += 2) {
+        step(IntC<0>{}, t, sa, sb);
+        step(IntC<1>{}, t + 1, sb, sa);
+    }
+    if (t < nt_w) {
+        step(IntC<0>{}, t, sa, sb);
+        ++t;
+    }
+    for (; t < ntiles; ++t) {
+        refill(t & 1, t);
+        wait_vmem_all();
+        __syncthreads();
+    }
+
+    // epilogue: O = o / l (0 for a row without keys), LSE = ms + log2 l in nats (-inf then)
+    const float lt = l + shfl_xor_f32(l, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qrow < N) {
+        uint16_t *orow = O + q_base + (size_t)qrow * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4_t w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2(acc[cb][8 * h + 2 * e] * inv, acc[cb][8 * h + 2 * e + 1] * inv);
+                *(u32x4_t *)(orow + 32 * cb + 16 * h + 8 * g) = w;
+            }
+        if (g == 0) LSE[(size_t)bh * N + qrow] = lt > 0.f ? (ms + log2_hw(lt)) * kLn2 : neg_inf();
     }
 }
 
