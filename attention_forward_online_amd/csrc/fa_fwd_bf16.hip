@@ -26,8 +26,11 @@
 //     3 of the row index swapped).  Then accumulator registers 8h..8h+7 of
 //     lane half g are keys 16h + 8g + 0..7: converted to bf16 they are the B
 //     operand of O^T = V^T P^T without any data movement.
-//   * K and V tiles are stored row-major in LDS alike; the V^T operand comes
-//     from the gfx950 transpose read (ds_read_b64_tr_b16), two per MFMA.
+//   * K and V tiles are stored row-major in LDS; the V^T operand comes from
+//     the gfx950 transpose read (ds_read_b64_tr_b16), two per MFMA.  The row
+//     strides differ: a transpose read serves 32 lanes per pass, four rows of
+//     16 banks each, and V's stride keeps those rows in disjoint banks (with
+//     K's stride they collided 2-way at d = 64 and 4-way at d = 128).
 //   * Scores stay fp32; exp runs as 2^(s*scale*log2 e - m'), one FMA plus
 //     v_exp_f32 per score; P is rounded to bf16 (RNE) only as the MFMA operand
 //     while the row sum uses the fp32 values.
@@ -63,7 +66,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
 constexpr int kBc = 64;                     // keys per K/V tile
-constexpr int kPad = 8;                     // bf16 pad per K/V row in LDS
+// LDS row strides (bf16 elements).  In 4-byte banks modulo 64: K rows step
+// by 4 x odd banks, so the 16 rows one ds_read_b128 pass reads (16 lanes) start
+// in distinct 4-bank groups; V rows step by 16 or 48 banks, so the four rows
+// one pass of ds_read_b64_tr_b16 reads (32 lanes, 16 banks per row) fall in
+// disjoint bank ranges.
+constexpr int kPadK = 8;
+constexpr int kPadV = 32;
 constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
 constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
 
@@ -76,8 +85,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
     float c) {
-    constexpr int KS = D + kPad;                // K and V row stride in LDS (elements)
-    constexpr int TILE = kBc * KS;              // elements per stage of K (or V)
+    constexpr int KS = D + kPadK;               // K row stride in LDS (elements)
+    constexpr int VS = D + kPadV;               // V row stride in LDS (elements)
+    static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "LDS strides off the bank pattern");
     constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
     constexpr int CB = D / 32;                  // 32-column blocks of O^T
     constexpr int NS = 2 * KK;                  // S MFMAs per tile (= P pairs made beside them)
@@ -88,8 +98,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
 
     // one array per stage, so that the stage a load fills and the stage the
     // MFMAs read are distinct objects
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE], Vs1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBc * KS], Ks1[kBc * KS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBc * VS], Vs1[kBc * VS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,22 +170,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
 
     // K/V tiles go from HBM straight into LDS (16-byte buffer loads with the
     // LDS flag: lane l of a wave's load fills bytes 16 l .. 16 l + 15 of a 1 KiB
-    // window).  A stage of KS-element rows is NJ such windows; wave w issues
-    // windows w, w + 4, ...  Each lane's global offset within the tile is fixed:
-    // its window position's row and 16-byte column, or an offset past every
-    // buffer for the row padding (the range check then writes zeros).
-    constexpr int RB = KS * 2;                  // LDS row bytes
-    constexpr int NJ = kBc * RB / 1024;         // 1 KiB windows per stage
-    constexpr int MJ = (NJ + kWaves - 1) / kWaves;
-    static_assert(NJ * 1024 == kBc * RB, "stage is not a whole number of windows");
-    uint32_t goff[MJ];
+    // window).  A stage of rows of RS elements is a whole number of such
+    // windows; wave w issues windows w, w + 4, ...  Each lane's global offset
+    // within the tile is fixed: its window position's row and 16-byte column,
+    // or an offset past every buffer for the row padding (the range check then
+    // writes zeros).
+    auto window_offsets = [&](auto rs_c, uint32_t *goff) {
+        constexpr int RB = decltype(rs_c)::value * 2;   // LDS row bytes
+        constexpr int NJ = kBc * RB / 1024, MJ = (NJ + kWaves - 1) / kWaves;
 #pragma unroll
-    for (int m = 0; m < MJ; ++m) {
-        const int p = 1024 * (wave + kWaves * m) + 16 * lane;
-        const int r = p / RB, q = (p % RB) / 16;
-        goff[m] = (q < D / 8 && r < kBc) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
-    }
-    auto dma = [&](const uint16_t *src, uint16_t *dst, int t) {
+        for (int m = 0; m < MJ; ++m) {
+            const int p = 1024 * (wave + kWaves * m) + 16 * lane;
+            const int r = p / RB, q = (p % RB) / 16;
+            goff[m] = (q < D / 8 && r < kBc) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
+        }
+    };
+    constexpr int NJK = kBc * KS * 2 / 1024, NJV = kBc * VS * 2 / 1024;
+    constexpr int MJK = (NJK + kWaves - 1) / kWaves, MJV = (NJV + kWaves - 1) / kWaves;
+    static_assert(NJK * 1024 == kBc * KS * 2 && NJV * 1024 == kBc * VS * 2,
+                  "stage is not a whole number of windows");
+    uint32_t goffk[MJK], goffv[MJV];
+    window_offsets(IntC<KS>{}, goffk);
+    window_offsets(IntC<VS>{}, goffv);
+    auto dma = [&](auto nj_c, const uint32_t *goff, const uint16_t *src, uint16_t *dst, int t) {
+        constexpr int NJ = decltype(nj_c)::value, MJ = (NJ + kWaves - 1) / kWaves;
         const int j0 = t * kBc;
         const rsrc_t r = make_rsrc(src + (size_t)j0 * D, (uint32_t)max(kv_end - j0, 0) * D * 2);
 #pragma unroll
@@ -183,7 +201,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
             if (wave + kWaves * m < NJ)
                 buffer_load_lds16(r, (char *)dst + 1024 * (wave + kWaves * m), goff[m]);
     };
-    const uint16_t *kg = K + kv_base, *vg = V + kv_base;
+    auto dma_k = [&](uint16_t *dst, int t) { dma(IntC<NJK>{}, goffk, K + kv_base, dst, t); };
+    auto dma_v = [&](uint16_t *dst, int t) { dma(IntC<NJV>{}, goffv, V + kv_base, dst, t); };
     // operand of S MFMA i (block jb = i % 2, k-step kk = i / 2) from the K tile in `stage`
     auto k_operand = [&](int stage, int i) {
         const int jb = i & 1, kk = i >> 1;
@@ -193,9 +212,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     auto v_operand = [&](int stage, int i) {
         const int ci = i / CB, cb = i % CB, jb = ci >> 1, h = ci & 1;
         const auto *p0 = (const __attribute__((address_space(3))) uint16_t *)vst(stage) +
-                         (8 * g + vrow + 32 * jb + 16 * h) * KS + vcol + 32 * cb;
+                         (8 * g + vrow + 32 * jb + 16 * h) * VS + vcol + 32 * cb;
         const u32x2_t lo = lds_read_tr16(p0);
-        const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
+        const u32x2_t hi = lds_read_tr16(p0 + 4 * VS);
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
     // P pair q (chunk q / 4, scores 2(q % 4), +1 of it): 2^(s c - ref) in fp32 into the
@@ -248,9 +267,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     };
 
     // prologue: K(0), V(0), K(1) into LDS, then S(0) prepared
-    dma(kg, Ks0, 0);
-    dma(vg, Vs0, 0);
-    dma(kg, Ks1, 1);
+    dma_k(Ks0, 0);
+    dma_v(Vs0, 0);
+    dma_k(Ks1, 1);
     wait_vmem_all();
     __syncthreads();
     f32x16_t sa[2], sb[2];
@@ -273,8 +292,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     // products are computed but not used (the stage then holds zeros or
     // another wave's next tile).
     auto refill = [&](int par, int t) {   // K(t+2), V(t+1); they land before the barrier
-        dma(kg, kst(par), t + 2);
-        dma(vg, vst(par ^ 1), t + 1);
+        dma_k(kst(par), t + 2);
+        dma_v(vst(par ^ 1), t + 1);
     };
     auto step = [&](auto par_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         constexpr int par = decltype(par_c)::value;
