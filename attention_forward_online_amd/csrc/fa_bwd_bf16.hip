@@ -35,7 +35,18 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBq = 128;     // queries per dQ workgroup (32 per wave)
 constexpr int kBk = 128;     // keys per dK/dV workgroup (32 per wave)
 constexpr int kTile = 64;    // keys per K/V tile (dQ) and queries per Q/dO tile (dK/dV)
-constexpr int kPad = 8;      // bf16 pad per LDS row
+
+// LDS row stride (bf16 elements) of the Q, dO, K and V tiles.  Each tile is
+// read two ways: 16-byte row reads (16 lanes per LDS pass, 16 different rows,
+// conflict-free when rows step by 4 x odd banks modulo 64) and
+// ds_read_b64_tr_b16 (32 lanes per pass: four consecutive rows of 16 banks
+// each).  No stride serves both without conflicts; d = 64 rows step by 36
+// banks (transpose reads 2-way), d = 128 rows by 76 = 12 mod 64 (transpose
+// reads 2-way instead of the 4-way of a 16-byte pad).  An XOR swizzle that is
+// conflict-free for both measured slower at d = 64 (more address registers).
+template <int D> constexpr int kRowElems = D == 64 ? D + 8 : D + 24;
+template <int D>
+__device__ __forceinline__ int lds_at(int row, int col) { return row * kRowElems<D> + col; }
 
 // Workgroup -> (head, block rank); with B*H divisible by 8 all blocks of a
 // head run on one XCD (round-robin dispatch), as in the forward.
@@ -104,8 +115,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_qtiles,
     int xcd_interleave, float c, float scale) {
     constexpr int NST = 2;
-    constexpr int KS = D + kPad;
-    constexpr int TILE = kTile * KS;
+    constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
     constexpr int KL = kTile * D / 8 / kThreads;
@@ -181,8 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int p = 0; p < KL; ++p) {
             const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            *(u32x4_t *)&Ks[stage * TILE + row * KS + 8 * col8] = kr[p];
-            *(u32x4_t *)&Vs[stage * TILE + row * KS + 8 * col8] = vr[p];
+            *(u32x4_t *)&Ks[stage * TILE + lds_at<D>(row, 8 * col8)] = kr[p];
+            *(u32x4_t *)&Vs[stage * TILE + lds_at<D>(row, 8 * col8)] = vr[p];
         }
     };
     auto active = [&](int t) {
@@ -193,17 +203,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     auto rows_times = [&](const uint16_t *R, int stage, const u32x4_t (&F)[KK], f32x16_t (&s)[2]) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const uint16_t *rp = &R[stage * TILE + (32 * jb + krow) * KS + 8 * g];
-            s[jb] = mfma32(*(const u32x4_t *)rp, F[0], f32x16_t{});
+            const uint16_t *rp = &R[stage * TILE];
+            s[jb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * jb + krow, 8 * g)], F[0], f32x16_t{});
 #pragma unroll
             for (int kk = 1; kk < KK; ++kk)
-                s[jb] = mfma32(*(const u32x4_t *)(rp + 16 * kk), F[kk], s[jb]);
+                s[jb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * jb + krow, 16 * kk + 8 * g)], F[kk], s[jb]);
         }
     };
     auto kt_operand = [&](int stage, int cb, int jb, int h) {
-        const auto *p0 = ks_lds + stage * TILE + (8 * g + trow + 32 * jb + 16 * h) * KS + tcol + 32 * cb;
-        const u32x2_t lo = lds_read_tr16(p0);
-        const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
+        const int r0 = 8 * g + trow + 32 * jb + 16 * h;
+        const u32x2_t lo = lds_read_tr16(ks_lds + stage * TILE + lds_at<D>(r0, tcol + 32 * cb));
+        const u32x2_t hi = lds_read_tr16(ks_lds + stage * TILE + lds_at<D>(r0 + 4, tcol + 32 * cb));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
 
@@ -282,8 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_ktiles,
     int xcd_interleave, float c, float scale) {
     constexpr int NST = 2;
-    constexpr int KS = D + kPad;
-    constexpr int TILE = kTile * KS;
+    constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
     constexpr int KL = kTile * D / 8 / kThreads;
@@ -369,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int p = 0; p < KL; ++p) {
             const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            *(u32x4_t *)&Qs[stage * TILE + row * KS + 8 * col8] = qr[p];
-            *(u32x4_t *)&Gs[stage * TILE + row * KS + 8 * col8] = gr[p];
+            *(u32x4_t *)&Qs[stage * TILE + lds_at<D>(row, 8 * col8)] = qr[p];
+            *(u32x4_t *)&Gs[stage * TILE + lds_at<D>(row, 8 * col8)] = gr[p];
         }
         if (tid < 16) *(u32x4_t *)&Ls[stage * kTile + 4 * tid] = lr;
         else if (tid < 32) *(u32x4_t *)&Ds[stage * kTile + 4 * (tid - 16)] = lr;
@@ -385,20 +394,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     auto rows_times = [&](const uint16_t *R, int stage, const u32x4_t (&F)[KK], f32x16_t (&s)[2]) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const uint16_t *rp = &R[stage * TILE + (32 * qb + qperm) * KS + 8 * g];
-            s[qb] = mfma32(*(const u32x4_t *)rp, F[0], f32x16_t{});
+            const uint16_t *rp = &R[stage * TILE];
+            s[qb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * qb + qperm, 8 * g)], F[0], f32x16_t{});
 #pragma unroll
             for (int kk = 1; kk < KK; ++kk)
-                s[qb] = mfma32(*(const u32x4_t *)(rp + 16 * kk), F[kk], s[qb]);
+                s[qb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * qb + qperm, 16 * kk + 8 * g)], F[kk], s[qb]);
         }
     };
     // transpose read of a Q or dO tile: lane li gets column 32cb + perm32(li)
     // of queries 32qb + 16h + 8g + 0..7
     auto t_operand = [&](const __attribute__((address_space(3))) uint16_t *base, int stage, int cb,
                          int qb, int h) {
-        const auto *p0 = base + stage * TILE + (8 * g + trow + 32 * qb + 16 * h) * KS + tcol + 32 * cb;
-        const u32x2_t lo = lds_read_tr16(p0);
-        const u32x2_t hi = lds_read_tr16(p0 + 4 * KS);
+        const int r0 = 8 * g + trow + 32 * qb + 16 * h;
+        const u32x2_t lo = lds_read_tr16(base + stage * TILE + lds_at<D>(r0, tcol + 32 * cb));
+        const u32x2_t hi = lds_read_tr16(base + stage * TILE + lds_at<D>(r0 + 4, tcol + 32 * cb));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
 
