@@ -24,6 +24,11 @@
 //                     dK and dV rows.
 // Masking follows the forward exactly: causal key j <= i + (Nk - N), keys at
 // or past key_lens[b] invisible; invisible pairs get P = 0, hence dS = 0.
+// Both streaming kernels load their tiles from HBM straight into LDS (buffer
+// loads with the LDS flag, one tile ahead, two stages held in separate arrays)
+// and pipeline each tile by halves: the MFMAs that produce S and dP of the
+// second 32-row block run beside the exponentials of the first, and the
+// gradient MFMAs of the first block beside the exponentials of the second.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -44,6 +49,8 @@ constexpr int kTile = 64;    // keys per K/V tile (dQ) and queries per Q/dO tile
 // banks (transpose reads 2-way), d = 128 rows by 76 = 12 mod 64 (transpose
 // reads 2-way instead of the 4-way of a 16-byte pad).  An XOR swizzle that is
 // conflict-free for both measured slower at d = 64 (more address registers).
+template <int N_> struct IntC { static constexpr int value = N_; };
+
 template <int D> constexpr int kRowElems = D == 64 ? D + 8 : D + 24;
 template <int D>
 __device__ __forceinline__ int lds_at(int row, int col) { return row * kRowElems<D> + col; }
@@ -114,25 +121,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const float *__restrict__ L2, const float *__restrict__ Dd,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_qtiles,
     int xcd_interleave, float c, float scale) {
-    constexpr int NST = 2;
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
-    constexpr int KL = kTile * D / 8 / kThreads;
-    static_assert(kTile * D / 8 % kThreads == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[NST * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[NST * TILE];
+    // one array per stage: the stage being loaded and the stage being read
+    // are distinct objects, so no LDS read waits for the loads in flight
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE], Vs1[TILE];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < kWaves);
     const int li = lane & 31, g = lane >> 5;
     const int krow = perm32(li);
     // K^T operand through the transpose read (the forward's V^T read): lane li
     // receives K column perm32(li) of 4 consecutive keys per read
     const int trow = (li & 15) >> 2;
     const int tcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    const __attribute__((address_space(3))) uint16_t *ks_lds =
-        (const __attribute__((address_space(3))) uint16_t *)&Ks[0];
+    auto kst = [&](int stage) -> uint16_t * { return stage ? Ks1 : Ks0; };
+    auto vst = [&](int stage) -> uint16_t * { return stage ? Vs1 : Vs0; };
 
     int bh, rank;
     block_of(blockIdx.x, n_qtiles, xcd_interleave, bh, rank);
@@ -153,8 +161,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
     const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);
     const rsrc_t dosrc = make_rsrc(dO + q_base, (uint32_t)N * D * 2);
-    const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)max(kv_end, 0) * D * 2);
-    const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)max(kv_end, 0) * D * 2);
 
     u32x4_t qf[KK], dof[KK];
 #pragma unroll
@@ -176,93 +182,133 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
 
-    u32x4_t kr[KL], vr[KL];
-    auto gload = [&](int t) {
+    // K/V tiles go from HBM straight into LDS: lane l of a wave's 16-byte
+    // LDS load fills bytes 16 l .. 16 l + 15 of a 1 KiB window; a stage of
+    // padded rows is NJ windows, wave w issues windows w, w + 4, ...  Each
+    // lane's offset inside a tile is fixed (its window slot's row and 16-byte
+    // column, or an out-of-range offset for the row padding: zeros).
+    constexpr int RB = kRowElems<D> * 2;
+    constexpr int NJ = kTile * RB / 1024, MJ = (NJ + kWaves - 1) / kWaves;
+    static_assert(NJ * 1024 == kTile * RB, "stage is not a whole number of windows");
+    uint32_t goff[MJ];
+#pragma unroll
+    for (int m = 0; m < MJ; ++m) {
+        const int p = 1024 * (wave + kWaves * m) + 16 * lane;
+        const int r = p / RB, q = (p % RB) / 16;
+        goff[m] = (q < D / 8 && r < kTile) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
+    }
+    auto refill = [&](int t, int stage) {
         const int j0 = t * kTile;
+        const uint32_t bytes = (uint32_t)max(kv_end - j0, 0) * D * 2;
+        const rsrc_t kr = make_rsrc(K + kv_base + (size_t)j0 * D, bytes);
+        const rsrc_t vr = make_rsrc(V + kv_base + (size_t)j0 * D, bytes);
 #pragma unroll
-        for (int p = 0; p < KL; ++p) {
-            const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            const uint32_t off_b = (uint32_t)((j0 + row) * D + 8 * col8) * 2;
-            kr[p] = buffer_load16(ksrc, off_b);
-            vr[p] = buffer_load16(vsrc, off_b);
-        }
-    };
-    auto lstore = [&](int stage) {
-#pragma unroll
-        for (int p = 0; p < KL; ++p) {
-            const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            *(u32x4_t *)&Ks[stage * TILE + lds_at<D>(row, 8 * col8)] = kr[p];
-            *(u32x4_t *)&Vs[stage * TILE + lds_at<D>(row, 8 * col8)] = vr[p];
-        }
+        for (int m = 0; m < MJ; ++m)
+            if (wave + kWaves * m < NJ) {
+                buffer_load_lds16(kr, (char *)kst(stage) + 1024 * (wave + kWaves * m), goff[m]);
+                buffer_load_lds16(vr, (char *)vst(stage) + 1024 * (wave + kWaves * m), goff[m]);
+            }
     };
     auto active = [&](int t) {
         return wq_first <= wq_last && (!CAUSAL || t * kTile <= wq_last + off);
     };
-    // X^T = R F^T for one 64-key tile: R rows (keys, perm32 order) from LDS,
-    // F the per-lane query fragment
-    auto rows_times = [&](const uint16_t *R, int stage, const u32x4_t (&F)[KK], f32x16_t (&s)[2]) {
+    // X^T = R F^T for one 32-key block jb of the tile: R rows (keys, perm32
+    // order) from LDS, F the per-lane query fragment
+    auto row_operand = [&](const uint16_t *R, int jb, int kk) {
+        return *(const u32x4_t *)&R[lds_at<D>(32 * jb + krow, 16 * kk + 8 * g)];
+    };
+    auto rows_block = [&](const uint16_t *R, const u32x4_t (&F)[KK], int jb, f32x16_t &x) {
+        x = mfma32(row_operand(R, jb, 0), F[0], f32x16_t{});
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const uint16_t *rp = &R[stage * TILE];
-            s[jb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * jb + krow, 8 * g)], F[0], f32x16_t{});
-#pragma unroll
-            for (int kk = 1; kk < KK; ++kk)
-                s[jb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * jb + krow, 16 * kk + 8 * g)], F[kk], s[jb]);
-        }
+        for (int kk = 1; kk < KK; ++kk) x = mfma32(row_operand(R, jb, kk), F[kk], x);
     };
     auto kt_operand = [&](int stage, int cb, int jb, int h) {
+        const auto *kb = (const __attribute__((address_space(3))) uint16_t *)kst(stage);
         const int r0 = 8 * g + trow + 32 * jb + 16 * h;
-        const u32x2_t lo = lds_read_tr16(ks_lds + stage * TILE + lds_at<D>(r0, tcol + 32 * cb));
-        const u32x2_t hi = lds_read_tr16(ks_lds + stage * TILE + lds_at<D>(r0 + 4, tcol + 32 * cb));
+        const u32x2_t lo = lds_read_tr16(kb + lds_at<D>(r0, tcol + 32 * cb));
+        const u32x2_t hi = lds_read_tr16(kb + lds_at<D>(r0 + 4, tcol + 32 * cb));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
 
-    gload(0);
-    lstore(0);
-    gload(1);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
+    // tile t is read from stage t % 2 while tile t + 1 loads into the other;
+    // unrolled by two so that both stages are compile-time objects
+    auto tile = [&](auto par_c, int t) {
+        constexpr int cur = decltype(par_c)::value;
+        refill(t + 1, cur ^ 1);   // lands before this iteration's barrier
         if (active(t)) {
             f32x16_t s[2], dp[2];
-            rows_times(Ks, cur, qf, s);
-            rows_times(Vs, cur, dof, dp);
+            uint32_t pk[2][8];
             const int j0 = t * kTile;
             const bool need_mask = (j0 + kTile > kv_lim) || (CAUSAL && j0 + kTile - 1 > wq_first + off);
-            if (need_mask) {
-                // register v of block jb holds key j0 + 32jb + 16(v/8) + 8g + v%8
-                const int vis_end = CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim;
-                const int lim = vis_end - j0 - 8 * g;
+            // P and dS of keys 2e, 2e + 1 of block jb, as the bf16 pair that
+            // feeds dQ^T += K^T dS^T
+            auto ds_pair = [&](int jb, int e) {
+                const int v = 2 * e;
+                const float p0 = exp2_hw(fmaf(s[jb][v], c, -l2));
+                const float p1 = exp2_hw(fmaf(s[jb][v + 1], c, -l2));
+                pk[jb][e] = pack_bf16x2(p0 * (dp[jb][v] - dd), p1 * (dp[jb][v + 1] - dd));
+                pin(pk[jb][e]);
+            };
+            auto dq_mfma = [&](int cb, int jb, int h, const u32x4_t &kt) {
+                acc[cb] = mfma32(kt, u32x4_t{pk[jb][4 * h], pk[jb][4 * h + 1], pk[jb][4 * h + 2], pk[jb][4 * h + 3]},
+                                 acc[cb]);
+            };
+            // keys at or past this lane's limit are invisible; register v of block
+            // jb holds key j0 + 32jb + 16(v/8) + 8g + v%8
+            const int lim = (CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim) - j0 - 8 * g;
+            auto mask_block = [&](int jb) {
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
+                for (int v = 0; v < 16; ++v)
+                    if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) s[jb][v] = neg_inf();
+            };
+            // half-tile pipeline: the S, dP MFMAs of key block 1 run beside the
+            // P, dS of block 0, and the dQ MFMAs of block 0 beside the P, dS of
+            // block 1 (each accumulator sums in the same order as a plain loop)
+            rows_block(kst(cur), qf, 0, s[0]);
+            rows_block(vst(cur), dof, 0, dp[0]);
+            if (need_mask) mask_block(0);
+            constexpr int NB = 2 * KK;
+            u32x4_t ra[2];
+            ra[0] = row_operand(kst(cur), 1, 0);
+            ra[1] = row_operand(vst(cur), 1, 0);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) s[jb][v] = neg_inf();
+            for (int i = 0; i < NB; ++i) {
+                const int kk = i >> 1;
+                const u32x4_t a = ra[i & 1];
+                if (i + 2 < NB) ra[i & 1] = row_operand((i & 1) ? vst(cur) : kst(cur), 1, kk + 1);
+                if (i & 1) dp[1] = mfma32(a, dof[kk], kk == 0 ? f32x16_t{} : dp[1]);
+                else s[1] = mfma32(a, qf[kk], kk == 0 ? f32x16_t{} : s[1]);
+#pragma unroll
+                for (int e = 8 * i / NB; e < 8 * (i + 1) / NB; ++e) ds_pair(0, e);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            uint32_t pk[2][8];
+            if (need_mask) mask_block(1);
+            constexpr int NQ = 2 * CB;
+            u32x4_t kt = kt_operand(cur, 0, 0, 0);
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
+            for (int i = 0; i < NQ; ++i) {
+                const u32x4_t a = kt;
+                if (i + 1 < NQ) kt = kt_operand(cur, (i + 1) >> 1, 0, (i + 1) & 1);
+                dq_mfma(i >> 1, 0, i & 1, a);
 #pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const float p0 = exp2_hw(fmaf(s[jb][v], c, -l2));
-                    const float p1 = exp2_hw(fmaf(s[jb][v + 1], c, -l2));
-                    pk[jb][v >> 1] = pack_bf16x2(p0 * (dp[jb][v] - dd), p1 * (dp[jb][v + 1] - dd));
-                }
+                for (int e = 8 * i / NQ; e < 8 * (i + 1) / NQ; ++e) ds_pair(1, e);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        acc[cb] = mfma32(kt_operand(cur, cb, jb, h),
-                                         u32x4_t{pk[jb][4 * h], pk[jb][4 * h + 1], pk[jb][4 * h + 2],
-                                                 pk[jb][4 * h + 3]},
-                                         acc[cb]);
+            for (int i = 0; i < NQ; ++i) dq_mfma(i >> 1, 1, i & 1, kt_operand(cur, i >> 1, 1, i & 1));
         }
-        lstore(cur ^ 1);
-        gload(t + 2);
+        wait_vmem_all();
         __syncthreads();
+    };
+    refill(0, 0);
+    wait_vmem_all();
+    __syncthreads();
+    int t = 0;
+    for (; t + 2 <= ntiles; t += 2) {
+        tile(IntC<0>{}, t);
+        tile(IntC<1>{}, t + 1);
     }
+    if (t < ntiles) tile(IntC<0>{}, t);
 
     if (qrow < N) {
         uint16_t *grow = dQ + q_base + (size_t)qrow * D;
@@ -291,28 +337,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     uint16_t *__restrict__ dV, const float *__restrict__ L2, const float *__restrict__ Dd,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_ktiles,
     int xcd_interleave, float c, float scale) {
-    constexpr int NST = 2;
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
-    constexpr int KL = kTile * D / 8 / kThreads;
     constexpr bool WANT_DV = MODE != kOnlyDK, WANT_DK = MODE != kOnlyDV;
-    static_assert(kTile * D / 8 % kThreads == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[NST * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Gs[NST * TILE];   // dO
-    __shared__ __attribute__((aligned(16))) float Ls[NST * kTile];
-    __shared__ __attribute__((aligned(16))) float Ds[NST * kTile];
+    // one array per stage (see the dQ kernel); LD holds the tile's 64 LSE2
+    // values followed by its 64 D values
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE], Qs1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Gs0[TILE], Gs1[TILE];   // dO
+    __shared__ __attribute__((aligned(16))) float LD0[2 * kTile], LD1[2 * kTile];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave >= 0 && wave < kWaves);
     const int li = lane & 31, g = lane >> 5;
     const int qperm = perm32(li);
     const int trow = (li & 15) >> 2;
     const int tcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    const __attribute__((address_space(3))) uint16_t *qs_lds =
-        (const __attribute__((address_space(3))) uint16_t *)&Qs[0];
-    const __attribute__((address_space(3))) uint16_t *gs_lds =
-        (const __attribute__((address_space(3))) uint16_t *)&Gs[0];
+    auto qst = [&](int stage) -> uint16_t * { return stage ? Qs1 : Qs0; };
+    auto gst = [&](int stage) -> uint16_t * { return stage ? Gs1 : Gs0; };
+    auto ldst = [&](int stage) -> float * { return stage ? LD1 : LD0; };
 
     int bh, rank;
     block_of(blockIdx.x, n_ktiles, xcd_interleave, bh, rank);
@@ -336,8 +381,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
     const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)Nk * D * 2);
     const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)Nk * D * 2);
-    const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);
-    const rsrc_t gsrc = make_rsrc(dO + q_base, (uint32_t)N * D * 2);
     // whole tiles of the padded per-head arrays: every 16-byte load is in range
     // or (prefetch past the last tile) entirely out of it
     const rsrc_t lsrc = make_rsrc(L2 + (size_t)bh * Npad, (uint32_t)Npad * 4);
@@ -360,124 +403,156 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
             adv[cb][v] = 0.f;
         }
 
-    u32x4_t qr[KL], gr[KL], lr = u32x4_t{0u, 0u, 0u, 0u};
-    auto gload = [&](int t) {
+    // Q/dO tiles go from HBM straight into LDS (as the K/V tiles of the dQ
+    // kernel); the tile's LSE2 and D values follow with one 16-lane load each
+    // (waves 0 and 1), into LD[0..63] and LD[64..127]
+    constexpr int RB = kRowElems<D> * 2;
+    constexpr int NJ = kTile * RB / 1024, MJ = (NJ + kWaves - 1) / kWaves;
+    static_assert(NJ * 1024 == kTile * RB, "stage is not a whole number of windows");
+    uint32_t goff[MJ];
+#pragma unroll
+    for (int m = 0; m < MJ; ++m) {
+        const int p = 1024 * (wave + kWaves * m) + 16 * lane;
+        const int r = p / RB, q = (p % RB) / 16;
+        goff[m] = (q < D / 8 && r < kTile) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
+    }
+    auto refill = [&](int t, int stage) {
         const int i0 = (t_first + t) * kTile;
+        const uint32_t bytes = (uint32_t)max(N - i0, 0) * D * 2;
+        const rsrc_t qr = make_rsrc(Q + q_base + (size_t)i0 * D, bytes);
+        const rsrc_t gr = make_rsrc(dO + q_base + (size_t)i0 * D, bytes);
 #pragma unroll
-        for (int p = 0; p < KL; ++p) {
-            const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            const uint32_t off_b = (uint32_t)((i0 + row) * D + 8 * col8) * 2;
-            qr[p] = buffer_load16(qsrc, off_b);
-            gr[p] = buffer_load16(gsrc, off_b);
-        }
-        // threads 0..15: L2 of the tile's 64 queries, 16..31: D
-        if (tid < 16) lr = buffer_load16(lsrc, (uint32_t)(i0 + 4 * tid) * 4);
-        else if (tid < 32) lr = buffer_load16(dsrc, (uint32_t)(i0 + 4 * (tid - 16)) * 4);
-    };
-    auto lstore = [&](int stage) {
-#pragma unroll
-        for (int p = 0; p < KL; ++p) {
-            const int e = tid + kThreads * p, row = e / (D / 8), col8 = e % (D / 8);
-            *(u32x4_t *)&Qs[stage * TILE + lds_at<D>(row, 8 * col8)] = qr[p];
-            *(u32x4_t *)&Gs[stage * TILE + lds_at<D>(row, 8 * col8)] = gr[p];
-        }
-        if (tid < 16) *(u32x4_t *)&Ls[stage * kTile + 4 * tid] = lr;
-        else if (tid < 32) *(u32x4_t *)&Ds[stage * kTile + 4 * (tid - 16)] = lr;
+        for (int m = 0; m < MJ; ++m)
+            if (wave + kWaves * m < NJ) {
+                buffer_load_lds16(qr, (char *)qst(stage) + 1024 * (wave + kWaves * m), goff[m]);
+                buffer_load_lds16(gr, (char *)gst(stage) + 1024 * (wave + kWaves * m), goff[m]);
+            }
+        if (wave < 2 && lane < 16)
+            buffer_load_lds16(wave == 0 ? lsrc : dsrc, (char *)ldst(stage) + 256 * wave, (uint32_t)(i0 + 4 * lane) * 4);
     };
     // a wave works on a tile if a query of it sees this wave's first key
     auto active = [&](int t) {
         const int i_last = (t_first + t) * kTile + kTile - 1;
         return wk0 < kv_lim && (!CAUSAL || i_last + off >= wk0);
     };
-    // X = R F^T for the tile's 64 queries (two 32-query blocks, rows in
-    // perm32 order) against this lane's key fragment F
-    auto rows_times = [&](const uint16_t *R, int stage, const u32x4_t (&F)[KK], f32x16_t (&s)[2]) {
+    // X = R F^T for the 32-query block qb of the tile (rows in perm32 order)
+    // against this lane's key fragment F
+    auto row_operand = [&](const uint16_t *R, int qb, int kk) {
+        return *(const u32x4_t *)&R[lds_at<D>(32 * qb + qperm, 16 * kk + 8 * g)];
+    };
+    auto rows_block = [&](const uint16_t *R, const u32x4_t (&F)[KK], int qb, f32x16_t &x) {
+        x = mfma32(row_operand(R, qb, 0), F[0], f32x16_t{});
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const uint16_t *rp = &R[stage * TILE];
-            s[qb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * qb + qperm, 8 * g)], F[0], f32x16_t{});
-#pragma unroll
-            for (int kk = 1; kk < KK; ++kk)
-                s[qb] = mfma32(*(const u32x4_t *)&rp[lds_at<D>(32 * qb + qperm, 16 * kk + 8 * g)], F[kk], s[qb]);
-        }
+        for (int kk = 1; kk < KK; ++kk) x = mfma32(row_operand(R, qb, kk), F[kk], x);
     };
     // transpose read of a Q or dO tile: lane li gets column 32cb + perm32(li)
     // of queries 32qb + 16h + 8g + 0..7
-    auto t_operand = [&](const __attribute__((address_space(3))) uint16_t *base, int stage, int cb,
-                         int qb, int h) {
+    auto t_operand = [&](const uint16_t *T, int cb, int qb, int h) {
+        const auto *tb = (const __attribute__((address_space(3))) uint16_t *)T;
         const int r0 = 8 * g + trow + 32 * qb + 16 * h;
-        const u32x2_t lo = lds_read_tr16(base + stage * TILE + lds_at<D>(r0, tcol + 32 * cb));
-        const u32x2_t hi = lds_read_tr16(base + stage * TILE + lds_at<D>(r0 + 4, tcol + 32 * cb));
+        const u32x2_t lo = lds_read_tr16(tb + lds_at<D>(r0, tcol + 32 * cb));
+        const u32x2_t hi = lds_read_tr16(tb + lds_at<D>(r0 + 4, tcol + 32 * cb));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     };
 
-    gload(0);
-    lstore(0);
-    gload(1);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
+    // tile t is read from stage t % 2 while tile t + 1 loads into the other;
+    // within a tile the two 32-query blocks are software-pipelined as in the
+    // dQ kernel: the S, dP MFMAs of block 1 run beside the P, dS of block 0,
+    // the dV, dK MFMAs of block 0 beside the P, dS of block 1
+    auto tile = [&](auto par_c, int t) {
+        constexpr int cur = decltype(par_c)::value;
+        refill(t + 1, cur ^ 1);   // lands before this iteration's barrier
         if (active(t)) {
             const int i0 = (t_first + t) * kTile;
+            const uint16_t *Qc = qst(cur), *Gc = gst(cur);
+            const float *LDc = ldst(cur);
             f32x16_t s[2], dp[2];
-            rows_times(Qs, cur, kf, s);
-            if constexpr (WANT_DK) rows_times(Gs, cur, vf, dp);
-            // register v of block qb holds query i0 + 32qb + 16(v/8) + 8g + v%8
-            const bool need_mask =
-                !key_vis || (i0 + kTile > N) || (CAUSAL && i0 + off < wk0 + 31);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int i = i0 + 32 * qb + 16 * (v >> 3) + 8 * g + (v & 7);
-                        if (!key_vis || i >= N || (CAUSAL && key > i + off)) s[qb][v] = neg_inf();
-                    }
-            }
             uint32_t pp[2][8], pd[2][8];
+            // register v of block qb holds query i0 + 32qb + 16(v/8) + 8g + v%8
+            const bool need_mask = !key_vis || (i0 + kTile > N) || (CAUSAL && i0 + off < wk0 + 31);
+            auto mask_block = [&](int qb) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+                for (int v = 0; v < 16; ++v) {
+                    const int i = i0 + 32 * qb + 16 * (v >> 3) + 8 * g + (v & 7);
+                    if (!key_vis || i >= N || (CAUSAL && key > i + off)) s[qb][v] = neg_inf();
+                }
+            };
+            // LSE2 and D of the 16 queries block qb gives this lane
+            f32x4_t lv[4], dv[4];
+            auto load_ld = [&](int qb) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int i8 = 32 * qb + 16 * h + 8 * g;    // 8 consecutive queries
-                    const f32x4_t la = *(const f32x4_t *)&Ls[cur * kTile + i8];
-                    const f32x4_t lb = *(const f32x4_t *)&Ls[cur * kTile + i8 + 4];
-                    const f32x4_t da = *(const f32x4_t *)&Ds[cur * kTile + i8];
-                    const f32x4_t db = *(const f32x4_t *)&Ds[cur * kTile + i8 + 4];
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const int v = 8 * h + e;
-                        const float l0 = e < 4 ? la[e] : lb[e - 4], l1 = e < 4 ? la[e + 1] : lb[e - 3];
-                        const float d0 = e < 4 ? da[e] : db[e - 4], d1 = e < 4 ? da[e + 1] : db[e - 3];
-                        const float p0 = exp2_hw(fmaf(s[qb][v], c, -l0));
-                        const float p1 = exp2_hw(fmaf(s[qb][v + 1], c, -l1));
-                        if constexpr (WANT_DV) pp[qb][v >> 1] = pack_bf16x2(p0, p1);
-                        if constexpr (WANT_DK)
-                            pd[qb][v >> 1] = pack_bf16x2(p0 * (dp[qb][v] - d0), p1 * (dp[qb][v + 1] - d1));
-                    }
+                    const int i8 = 32 * qb + 16 * h + 8 * g;
+                    lv[2 * h] = *(const f32x4_t *)&LDc[i8];
+                    lv[2 * h + 1] = *(const f32x4_t *)&LDc[i8 + 4];
+                    dv[2 * h] = *(const f32x4_t *)&LDc[kTile + i8];
+                    dv[2 * h + 1] = *(const f32x4_t *)&LDc[kTile + i8 + 4];
                 }
+            };
+            // P (and dS) of queries 2e, 2e + 1 of block qb as bf16 pairs
+            auto p_pair = [&](int qb, int e) {
+                const int v = 2 * e;
+                const float l0 = lv[e >> 1][v & 3], l1 = lv[e >> 1][(v & 3) + 1];
+                const float d0 = dv[e >> 1][v & 3], d1 = dv[e >> 1][(v & 3) + 1];
+                const float p0 = exp2_hw(fmaf(s[qb][v], c, -l0));
+                const float p1 = exp2_hw(fmaf(s[qb][v + 1], c, -l1));
+                if constexpr (WANT_DV) {
+                    pp[qb][e] = pack_bf16x2(p0, p1);
+                    pin(pp[qb][e]);
+                }
+                if constexpr (WANT_DK) {
+                    pd[qb][e] = pack_bf16x2(p0 * (dp[qb][v] - d0), p1 * (dp[qb][v + 1] - d1));
+                    pin(pd[qb][e]);
+                }
+            };
+            auto grad_mfma = [&](int cb, int qb, int h) {
+                if constexpr (WANT_DV)
+                    adv[cb] = mfma32(t_operand(Gc, cb, qb, h),
+                                     u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2], pp[qb][4 * h + 3]},
+                                     adv[cb]);
+                if constexpr (WANT_DK)
+                    adk[cb] = mfma32(t_operand(Qc, cb, qb, h),
+                                     u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2], pd[qb][4 * h + 3]},
+                                     adk[cb]);
+            };
+            rows_block(Qc, kf, 0, s[0]);
+            if constexpr (WANT_DK) rows_block(Gc, vf, 0, dp[0]);
+            if (need_mask) mask_block(0);
+            load_ld(0);
+            // S (and dP) MFMAs of block 1, two P pairs of block 0 per S step
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+            for (int kk = 0; kk < KK; ++kk) {
+                s[1] = mfma32(row_operand(Qc, 1, kk), kf[kk], kk == 0 ? f32x16_t{} : s[1]);
+                if constexpr (WANT_DK) dp[1] = mfma32(row_operand(Gc, 1, kk), vf[kk], kk == 0 ? f32x16_t{} : dp[1]);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int e = 8 * kk / KK; e < 8 * (kk + 1) / KK; ++e) p_pair(0, e);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (need_mask) mask_block(1);
+            load_ld(1);
+            // dV, dK MFMAs of block 0 beside the P pairs of block 1
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        if constexpr (WANT_DV)
-                            adv[cb] = mfma32(t_operand(gs_lds, cur, cb, qb, h),
-                                             u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2],
-                                                     pp[qb][4 * h + 3]},
-                                             adv[cb]);
-                        if constexpr (WANT_DK)
-                            adk[cb] = mfma32(t_operand(qs_lds, cur, cb, qb, h),
-                                             u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2],
-                                                     pd[qb][4 * h + 3]},
-                                             adk[cb]);
-                    }
+            for (int i = 0; i < 2 * CB; ++i) {
+                grad_mfma(i >> 1, 0, i & 1);
+#pragma unroll
+                for (int e = 8 * i / (2 * CB); e < 8 * (i + 1) / (2 * CB); ++e) p_pair(1, e);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * CB; ++i) grad_mfma(i >> 1, 1, i & 1);
         }
-        lstore(cur ^ 1);
-        gload(t + 2);
+        wait_vmem_all();
         __syncthreads();
+    };
+    refill(0, 0);
+    wait_vmem_all();
+    __syncthreads();
+    int t = 0;
+    for (; t + 2 <= ntiles; t += 2) {
+        tile(IntC<0>{}, t);
+        tile(IntC<1>{}, t + 1);
     }
+    if (t < ntiles) tile(IntC<0>{}, t);
 
     // accumulator register 8h + e of block cb holds d = 32cb + 16h + 8g + e of this lane's key
     if (key < Nk) {
