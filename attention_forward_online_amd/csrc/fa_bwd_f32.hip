@@ -56,8 +56,8 @@ __device__ __forceinline__ float quad_dot(const float (&x)[NCH][4], const float 
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = fmaf(x[k][e], y[e], s);
     }
-    s += shfl_xor_f32(s, 1);
-    s += shfl_xor_f32(s, 2);
+    s += quad_xor_f32<1>(s);
+    s += quad_xor_f32<2>(s);
     return s;
 }
 
@@ -123,16 +123,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(
     const float l2 = qok ? L2[(size_t)bh * Npad + qrow] : 0.f;
     const float dd = qok ? Dd[(size_t)bh * Npad + qrow] : 0.f;
 
+    // K/V tiles: a thread's loads are issued at once, and up to DMAX = 64
+    // (where the registers allow it) the next tile's loads are in flight while
+    // one is computed
+    constexpr bool kPrefetch = DMAX <= 64;
+    const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
+    const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
+    F32TileStage<kT, DMAX, kThreads> kst, vst;
+    if (kPrefetch && ntiles > 0) {
+        kst.load(ksrc, 0, d, tid);
+        vst.load(vsrc, 0, d, tid);
+    }
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * kT;
-        __syncthreads();
-        for (int e = tid; e < kT * DMAX; e += kThreads) {
-            const int row = e / DMAX, col = e % DMAX, j = j0 + row;
-            const bool in = j < kv_end && col < d;
-            Ks[e] = in ? K[kv_base + (size_t)j * d + col] : 0.f;
-            Vs[e] = in ? V[kv_base + (size_t)j * d + col] : 0.f;
+        if (!kPrefetch) {
+            kst.load(ksrc, j0, d, tid);
+            vst.load(vsrc, j0, d, tid);
         }
         __syncthreads();
+        kst.store(Ks, tid);
+        vst.store(Vs, tid);
+        __syncthreads();
+        if (kPrefetch && t + 1 < ntiles) {
+            kst.load(ksrc, j0 + kT, d, tid);
+            vst.load(vsrc, j0 + kT, d, tid);
+        }
         for (int jj = 0; jj < kT; ++jj) {
             const float s = quad_dot<NCH>(q, &Ks[jj * DMAX], part);
             const float dp = quad_dot<NCH>(g, &Vs[jj * DMAX], part);
@@ -178,21 +193,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(
             dv[k][e] = 0.f;
         }
 
+    // Q/dO tiles (and their LSE2, D): loads issued at once; up to DMAX = 64
+    // the next tile's loads are in flight while one is computed
+    constexpr bool kPrefetch = DMAX <= 64;
+    const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * d * 4);
+    const rsrc_t gsrc = make_rsrc(dO + q_base, (uint32_t)N * d * 4);
+    const rsrc_t lsrc = make_rsrc(L2 + (size_t)bh * Npad, (uint32_t)N * 4);
+    const rsrc_t dsrc = make_rsrc(Dd + (size_t)bh * Npad, (uint32_t)N * 4);
+    F32TileStage<kT, DMAX, kThreads> qst, gst;
+    float lv = 0.f, dv2 = 0.f;
+    auto issue = [&](int i0) {
+        qst.load(qsrc, i0, d, tid);
+        gst.load(gsrc, i0, d, tid);
+        if (tid < kT) {
+            lv = buffer_load_f32(lsrc, (uint32_t)(i0 + tid) * 4);
+            dv2 = buffer_load_f32(dsrc, (uint32_t)(i0 + tid) * 4);
+        }
+    };
+    if (kPrefetch && ntiles > 0) issue(i_first);
     for (int t = 0; t < ntiles; ++t) {
         const int i0 = i_first + t * kT;
+        if (!kPrefetch) issue(i0);
         __syncthreads();
-        for (int e = tid; e < kT * DMAX; e += kThreads) {
-            const int row = e / DMAX, col = e % DMAX, i = i0 + row;
-            const bool in = i < N && col < d;
-            Qs[e] = in ? Q[q_base + (size_t)i * d + col] : 0.f;
-            Gs[e] = in ? dO[q_base + (size_t)i * d + col] : 0.f;
-        }
+        qst.store(Qs, tid);
+        gst.store(Gs, tid);
         if (tid < kT) {
-            const int i = i0 + tid;
-            Ls[tid] = i < N ? L2[(size_t)bh * Npad + i] : 0.f;
-            Ds[tid] = i < N ? Dd[(size_t)bh * Npad + i] : 0.f;
+            Ls[tid] = lv;
+            Ds[tid] = dv2;
         }
         __syncthreads();
+        if (kPrefetch && t + 1 < ntiles) issue(i0 + kT);
         for (int ii = 0; ii < kT; ++ii) {
             const int i = i0 + ii;
             const float s = quad_dot<NCH>(kr, &Qs[ii * DMAX], part);

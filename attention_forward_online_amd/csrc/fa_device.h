@@ -48,6 +48,35 @@ __device__ __forceinline__ u32x4_t buffer_load16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+__device__ __forceinline__ float buffer_load_f32(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// The share of a ROWS x DMAX fp32 tile (rows of `d` valid floats, zero-filled
+// to DMAX) that thread `tid` of a THREADS-thread workgroup copies from global
+// memory to LDS: elements tid + THREADS p.  load() only issues the loads, so a
+// caller can overlap them with work on the previous tile; a column at or past
+// d, or a row past the buffer's range, reads 0 (hardware range check).
+template <int ROWS, int DMAX, int THREADS>
+struct F32TileStage {
+    static constexpr int PER = ROWS * DMAX / THREADS;
+    static_assert(ROWS * DMAX % THREADS == 0, "tile/thread mismatch");
+    float v[PER];
+    __device__ __forceinline__ void load(rsrc_t src, int row0, int d, int tid) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + THREADS * p, row = e / DMAX, col = e % DMAX;
+            // a column at or past d gets an offset past any range (no branch)
+            const uint32_t off = (uint32_t)((row0 + row) * d + col) * 4u | (col < d ? 0u : 0xfffffff0u);
+            v[p] = buffer_load_f32(src, off);
+        }
+    }
+    __device__ __forceinline__ void store(float *lds, int tid) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) lds[tid + THREADS * p] = v[p];
+    }
+};
+
 // 16-byte buffer load straight into LDS (no register stage): lane l of the
 // wave writes bytes lds + 16 l .. lds + 16 l + 15; a lane whose offset fails the
 // range check writes zeros, an inactive lane writes nothing.  `lds` is
@@ -92,6 +121,15 @@ __device__ __forceinline__ float max_xor32(float v) {
 // Value of lane (lane ^ mask) for masks < 64.
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
     return __shfl_xor(v, mask, 64);
+}
+
+// Value of lane (lane ^ M) for M = 1 or 2: a DPP quad permutation on the VALU
+// (no LDS round trip, unlike a general shuffle).
+template <int M>
+__device__ __forceinline__ float quad_xor_f32(float v) {
+    static_assert(M == 1 || M == 2, "quad exchange");
+    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
 }
 
 // Row order of a 32-row MFMA operand block: operand row r reads row perm32(r)

@@ -49,32 +49,56 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
         }
     float ms = neg_inf(), l = 0.f;
 
+    // K/V tiles: all of a thread's loads are issued at once, and (up to
+    // DMAX = 64, where the registers allow it without losing a wave) the next
+    // tile's loads are in flight while the current one is computed
+    constexpr bool kPrefetch = DMAX <= 64;
+    const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
+    const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
+    F32TileStage<kBc, DMAX, kThreads> kst, vst;
+    if (kPrefetch && ntiles > 0) {
+        kst.load(ksrc, 0, d, tid);
+        vst.load(vsrc, 0, d, tid);
+    }
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * kBc;
-        __syncthreads();   // previous tile fully consumed
-        for (int e = tid; e < kBc * DMAX; e += kThreads) {
-            const int row = e / DMAX, col = e % DMAX, j = j0 + row;
-            const bool in = j < kv_end && col < d;
-            Ks[e] = in ? K[kv_base + (size_t)j * d + col] : 0.f;
-            Vs[e] = in ? V[kv_base + (size_t)j * d + col] : 0.f;
+        if (!kPrefetch) {
+            kst.load(ksrc, j0, d, tid);
+            vst.load(vsrc, j0, d, tid);
         }
+        __syncthreads();   // previous tile fully consumed
+        kst.store(Ks, tid);
+        vst.store(Vs, tid);
         __syncthreads();
+        if (kPrefetch && t + 1 < ntiles) {
+            kst.load(ksrc, j0 + kBc, d, tid);
+            vst.load(vsrc, j0 + kBc, d, tid);
+        }
 
+        // keys are taken in groups whose K rows are read from LDS in one batch
+        // (16 16-byte reads), so a wave waits once per group, not per key
+        constexpr int KG = NCH >= 16 ? 1 : 16 / NCH;
         float s[kBc];
 #pragma unroll
-        for (int jj = 0; jj < kBc; ++jj) {
-            float part_dot = 0.f;
+        for (int jg = 0; jg < kBc; jg += KG) {
+            f32x4_t kv[KG][NCH];
 #pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                const f32x4_t kv = *(const f32x4_t *)&Ks[jj * DMAX + 16 * k + 4 * part];
+            for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) part_dot = fmaf(q[k][e], kv[e], part_dot);
+                for (int k = 0; k < NCH; ++k) kv[u][k] = *(const f32x4_t *)&Ks[(jg + u) * DMAX + 16 * k + 4 * part];
+#pragma unroll
+            for (int u = 0; u < KG; ++u) {
+                float part_dot = 0.f;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) part_dot = fmaf(q[k][e], kv[u][k][e], part_dot);
+                part_dot += quad_xor_f32<1>(part_dot);
+                part_dot += quad_xor_f32<2>(part_dot);
+                const int key = j0 + jg + u;
+                const bool ok = key < kv_lim && (!causal || key <= qrow + off);
+                s[jg + u] = ok ? part_dot : neg_inf();
             }
-            part_dot += shfl_xor_f32(part_dot, 1);
-            part_dot += shfl_xor_f32(part_dot, 2);
-            const int key = j0 + jj;
-            const bool ok = key < kv_lim && (!causal || key <= qrow + off);
-            s[jj] = ok ? part_dot : neg_inf();
         }
         float mx = s[0];
 #pragma unroll
@@ -89,14 +113,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[k][e] *= alpha;
 #pragma unroll
-        for (int jj = 0; jj < kBc; ++jj) {
-            const float p = exp2_hw(fmaf(s[jj], c, -ms_ref));
-            l += p;
+        for (int jg = 0; jg < kBc; jg += KG) {
+            f32x4_t vv[KG][NCH];
 #pragma unroll
-            for (int k = 0; k < NCH; ++k) {
-                const f32x4_t vv = *(const f32x4_t *)&Vs[jj * DMAX + 16 * k + 4 * part];
+            for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[k][e] = fmaf(p, vv[e], o[k][e]);
+                for (int k = 0; k < NCH; ++k) vv[u][k] = *(const f32x4_t *)&Vs[(jg + u) * DMAX + 16 * k + 4 * part];
+#pragma unroll
+            for (int u = 0; u < KG; ++u) {
+                const float p = exp2_hw(fmaf(s[jg + u], c, -ms_ref));
+                l += p;
+#pragma unroll
+                for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[k][e] = fmaf(p, vv[u][k][e], o[k][e]);
             }
         }
     }
