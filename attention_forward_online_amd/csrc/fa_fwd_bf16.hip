@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     constexpr int NP2 = 4 * CB;                 // P.V MFMAs per tile
     constexpr int PAIRS2 = 16 - NS;             // P pairs left for the P.V section
     constexpr int PD = kPrefetch;
+    // the phase whose waves issue at raised priority (s_setprio 1): the P.V
+    // phase at d = 64, the S phase at d = 128 (measured: 2-3% each, the other
+    // choice neutral)
+    constexpr int kPrioPhase = D == 64 ? 2 : 1;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
 
     // one array per stage, so that the stage a load fills and the stage the
@@ -303,6 +307,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
         u32x4_t kop[PD];
 #pragma unroll
         for (int i = 0; i < PD; ++i) kop[i] = k_operand(par ^ 1, i);
+        if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
@@ -310,12 +315,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
             p_pair(sc, i, pk, rs);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(0);
         const bool more = t + 1 < nt_w;
         if (more && need_mask(t + 1)) apply_mask(t + 1, sn);
         float m4[4];
         u32x4_t vop[PD];
 #pragma unroll
         for (int i = 0; i < PD; ++i) vop[i] = v_operand(par, i);
+        if constexpr (kPrioPhase == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NP2; ++i) {
             const int ci = i / CB;
@@ -332,6 +339,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (kPrioPhase == 2) __builtin_amdgcn_s_setprio(0);
         l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         if (more) decide(rowmax(m4));
         wait_vmem_all();
