@@ -28,7 +28,9 @@
 // loads with the LDS flag, one tile ahead, two stages held in separate arrays)
 // and pipeline each tile by halves: the MFMAs that produce S and dP of the
 // second 32-row block run beside the exponentials of the first, and the
-// gradient MFMAs of the first block beside the exponentials of the second.
+// gradient MFMAs of the first block beside the exponentials of the second;
+// that last phase issues at raised wave priority (s_setprio 1: 5% at d = 64,
+// neutral at d = 128).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -284,6 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             }
             if (need_mask) mask_block(1);
             constexpr int NQ = 2 * CB;
+            __builtin_amdgcn_s_setprio(1);
             u32x4_t kt = kt_operand(cur, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
@@ -294,6 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 for (int e = 8 * i / NQ; e < 8 * (i + 1) / NQ; ++e) ds_pair(1, e);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int i = 0; i < NQ; ++i) dq_mfma(i >> 1, 1, i & 1, kt_operand(cur, i >> 1, 1, i & 1));
         }
@@ -531,6 +535,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
             if (need_mask) mask_block(1);
             load_ld(1);
             // dV, dK MFMAs of block 0 beside the P pairs of block 1
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < 2 * CB; ++i) {
                 grad_mfma(i >> 1, 0, i & 1);
@@ -538,6 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                 for (int e = 8 * i / (2 * CB); e < 8 * (i + 1) / (2 * CB); ++e) p_pair(1, e);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int i = 0; i < 2 * CB; ++i) grad_mfma(i >> 1, 1, i & 1);
         }
