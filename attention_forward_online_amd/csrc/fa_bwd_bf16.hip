@@ -9,12 +9,13 @@
 //     dS_ij = P_ij (dO_i . v_j - D_i)
 //     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
 //     dV_j = sum_i P_ij dO_i.
-// Three kernels, no atomics:
-//   bwd_prep_kernel   D_i and LSE_i in log2 units (0 for a row with no key).
+// Two kernels, no atomics:
 //   bwd_dq_kernel     one workgroup per 128 queries streams the K/V tiles (the
 //                     forward's shape): S^T = K Q^T and dP^T = V dO^T with the
 //                     query in the lane, then dQ^T += K^T dS^T with the K^T
-//                     operand from the LDS transpose read.
+//                     operand from the LDS transpose read.  It also computes
+//                     D_i and LSE_i in log2 units (0 for a row with no key) and
+//                     writes them for the second kernel.
 //   bwd_dkdv_kernel   one workgroup per 128 keys (K and V fragments stay in
 //                     VGPRs) streams the Q/dO tiles: S = Q K^T and dP = dO V^T
 //                     with the key in the lane; reading the Q/dO rows in perm32
@@ -71,58 +72,14 @@ __device__ __forceinline__ void block_of(int bid, int nblk, int xcd_interleave, 
     }
 }
 
-// D_i = dO_i . O_i and LSE_i * log2(e) (0 when LSE_i = -inf: that row sees no
-// key, so every one of its scores is masked anyway), into per-head arrays of
-// Npad = N rounded up to the 64-query tile; the padding gets zeros (its
-// queries are masked in every kernel).  D / 8 lanes per row.
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t *__restrict__ O,
-                                                            const uint16_t *__restrict__ dO,
-                                                            const float *__restrict__ LSE,
-                                                            float *__restrict__ L2,
-                                                            float *__restrict__ Dd, long long BH,
-                                                            int N, int Npad) {
-    constexpr int LPR = D / 8;
-    const long long prow = ((long long)blockIdx.x * kThreads + threadIdx.x) / LPR;
-    const int sub = threadIdx.x % LPR;
-    if (prow >= BH * Npad) return;   // whole row groups leave together
-    const long long bh = prow / Npad;
-    const int i = (int)(prow % Npad);
-    if (i >= N) {
-        if (sub == 0) {
-            Dd[prow] = 0.f;
-            L2[prow] = 0.f;
-        }
-        return;
-    }
-    const long long row = bh * N + i;
-    const u32x4_t o = *(const u32x4_t *)(O + row * D + 8 * sub);
-    const u32x4_t g = *(const u32x4_t *)(dO + row * D + 8 * sub);
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t ow = o[w], gw = g[w];
-        acc = fmaf(bf16_bits_to_f32(ow & 0xffffu), bf16_bits_to_f32(gw & 0xffffu), acc);
-        acc = fmaf(__builtin_bit_cast(float, ow & 0xffff0000u),
-                   __builtin_bit_cast(float, gw & 0xffff0000u), acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += shfl_xor_f32(acc, off);
-    if (sub == 0) {
-        const float lse = LSE[row];
-        Dd[prow] = acc;
-        L2[prow] = lse == neg_inf() ? 0.f : lse * kLog2e;
-    }
-}
-
 // dQ: 4 waves x 32 queries, K/V tiles of 64 keys through two LDS stages.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ,
-    const float *__restrict__ L2, const float *__restrict__ Dd,
-    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_qtiles,
-    int xcd_interleave, float c, float scale) {
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
+    const float *__restrict__ LSE, uint16_t *__restrict__ dQ, float *__restrict__ L2,
+    float *__restrict__ Dd, const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad,
+    int n_qtiles, int xcd_interleave, float c, float scale) {
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
@@ -164,17 +121,41 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const rsrc_t qsrc = make_rsrc(Q + q_base, (uint32_t)N * D * 2);
     const rsrc_t dosrc = make_rsrc(dO + q_base, (uint32_t)N * D * 2);
 
+    // Q and dO fragments stay in VGPRs; O is read once for D_i = dO_i . O_i
+    // (bf16 products exact in fp32, summed in fp32; lanes li and li + 32 hold
+    // the two halves of each 16-column chunk)
+    const rsrc_t osrc = make_rsrc(O + q_base, (uint32_t)N * D * 2);
     u32x4_t qf[KK], dof[KK];
+    float dpart = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        qf[kk] = buffer_load16(qsrc, (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2);
-        dof[kk] = buffer_load16(dosrc, (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2);
+        const uint32_t ob = (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2;
+        qf[kk] = buffer_load16(qsrc, ob);
+        dof[kk] = buffer_load16(dosrc, ob);
+        const u32x4_t of = buffer_load16(osrc, ob);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t ow = of[w], gw = dof[kk][w];
+            dpart = fmaf(bf16_bits_to_f32(ow & 0xffffu), bf16_bits_to_f32(gw & 0xffffu), dpart);
+            dpart = fmaf(__builtin_bit_cast(float, ow & 0xffff0000u),
+                         __builtin_bit_cast(float, gw & 0xffff0000u), dpart);
+        }
     }
-    // a query past N takes l2 = +inf: every P of its row is 0
-    float l2 = __builtin_inff(), dd = 0.f;
+    const float dd = dpart + shfl_xor_f32(dpart, 32);
+    // LSE in log2 units (0 when LSE = -inf: that row sees no key, so all of its
+    // scores are masked anyway); a query past N takes l2 = +inf: every P of its
+    // row is 0
+    float l2 = __builtin_inff();
     if (qrow < N) {
-        l2 = L2[(size_t)bh * Npad + qrow];
-        dd = Dd[(size_t)bh * Npad + qrow];
+        const float lse = LSE[(size_t)bh * N + qrow];
+        l2 = lse == neg_inf() ? 0.f : lse * kLog2e;
+    }
+    // D and LSE2 of the rows, for the dK/dV kernel that runs next, in per-head
+    // arrays of Npad = N rounded up to the 64-query tile; the padding gets
+    // zeros (its queries are masked there)
+    if (g == 0 && qrow < Npad) {
+        L2[(size_t)bh * Npad + qrow] = qrow < N ? l2 : 0.f;
+        Dd[(size_t)bh * Npad + qrow] = qrow < N ? dd : 0.f;
     }
     wait_vmem_all();
 
@@ -589,15 +570,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int xcd = (BH % 8 == 0) ? 1 : 0;
     const float c = a.scale * kLog2e;
     if (a.N > 0) {
-        const long long prows = BH * Npad;
-        const long long blocks = (prows * (D / 8) + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                           (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, L2, Dd, BH, a.N, Npad);
+        // the dQ kernel also writes the D and LSE2 arrays the dK/dV kernel reads
         const int n_qt = (a.N + kBq - 1) / kBq;
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qt)), dim3(kThreads), 0,
                            stream, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (const uint16_t *)a.dO, (uint16_t *)a.dQ, L2, Dd, a.key_lens, a.H, a.N,
-                           a.Nk, Npad, n_qt, xcd, c, a.scale);
+                           (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, (uint16_t *)a.dQ, L2,
+                           Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, xcd, c, a.scale);
     }
     if (a.Nk > 0) {
         const int n_kt = (a.Nk + kBk - 1) / kBk;

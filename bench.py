@@ -229,7 +229,7 @@ def main():
                          "peak": PEAK_BF16_TFLOPS,
                          "frac": round(bflops / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "unit": "TFLOP/s", "traffic": measured_traffic("backward/" + HEADLINE),
-                         "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel"},
+                         "kernels": "bwd_dq_kernel + bwd_dkdv_kernel"},
         }
         del dob, dq, dk, dv, wsb
         # ------------------------------------ V1 loop order (ablation), headline shape
