@@ -110,6 +110,15 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const __attribute__((address_sp
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N vector-memory loads of this wave are outstanding (they
+// complete in issue order for this count): s_waitcnt vmcnt(N), vmcnt split
+// over bits 3:0 and 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // max(v, value of lane ^ 32) on the VALU (v_permlane32_swap exchanges the
 // two 32-lane halves), without going through the LDS queue.
 __device__ __forceinline__ float max_xor32(float v) {

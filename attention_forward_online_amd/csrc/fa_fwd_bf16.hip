@@ -156,7 +156,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
         qf[kk] = buffer_load16(qsrc, (uint32_t)(qrow * D + 16 * kk + 8 * g) * 2);   // rows >= N read 0
-    wait_vmem_all();
 
     f32x16_t acc[CB];
 #pragma unroll
@@ -270,12 +269,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
         return max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
     };
 
-    // prologue: K(0), V(0), K(1) into LDS, then S(0) prepared
+    // prologue: K(0), V(0), K(1) into LDS, issued with the Q loads; S(0) is
+    // prepared as soon as Q and K(0) have landed (every wave has at most its
+    // V(0) and K(1) windows outstanding), the rest arrives meanwhile
     dma_k(Ks0, 0);
     dma_v(Vs0, 0);
     dma_k(Ks1, 1);
-    wait_vmem_all();
-    __syncthreads();
+    wait_vmem_le<NJV / kWaves + NJK / kWaves>();
+    // every wave's K(0) windows are in LDS; the barrier carries no release
+    // fence (that would wait for V(0) and K(1) too), the acquire fence keeps
+    // the LDS reads below it
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     f32x16_t sa[2], sb[2];
     if (nt_w > 0) {
 #pragma unroll
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
         for (int k = 0; k < 4; ++k) m4[k] = max8(sa, k);
         decide(rowmax(m4));
     }
+    wait_vmem_all();
     __syncthreads();
 
     // iteration t: K(t+2) and V(t+1) are loaded into the stages K(t) and
