@@ -3,11 +3,14 @@
 // The same tile recurrence as the bf16 path ('Online Softmax -- the
 // mathematical heart of FlashAttention', sections 4-5), with every product and
 // sum in fp32 on the vector ALUs: no reduced-precision matrix instruction
-// touches the data.  One workgroup holds 64 query rows; four lanes share a row
-// and split its d dimension in 4-float pieces, so a score is four partial dot
-// products combined by two lane exchanges inside the quad.  K/V tiles of 32
-// keys are staged in LDS, zero-padded to the compiled width DMAX (zeros add
-// nothing to a dot product and the padded output columns are never stored).
+// touches the data.  LPR lanes share a query row and split its d dimension in
+// 4-float pieces, so a score is LPR partial dot products combined by lane
+// exchanges (DPP) inside the row's lane group; a workgroup of 256 threads holds
+// 256 / LPR rows.  LPR = 4 in general; small grids (a few workgroups, e.g. one
+// 256-row head) take LPR = 16, which gives four times the waves and a quarter
+// of the per-lane work per key.  K/V tiles of 32 keys are staged in LDS,
+// zero-padded to the compiled width DMAX (zeros add nothing to a dot product
+// and the padded output columns are never stored).
 // Fully masked rows give O = 0 and LSE = -inf as in the bf16 path.
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -16,21 +19,34 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = kThreads / 4;   // query rows per workgroup
 constexpr int kBc = 32;               // keys per tile
 
-template <int DMAX>
+// sum over the LPR lanes of a row group (LPR = 4: quad; 16: DPP row)
+template <int LPR>
+__device__ __forceinline__ float row_group_sum(float x) {
+    if constexpr (LPR == 16) {
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));   // row_ror:8
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));   // row_ror:4
+    }
+    x += quad_xor_f32<1>(x);
+    x += quad_xor_f32<2>(x);
+    return x;
+}
+
+template <int DMAX, int LPR>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ key_lens,
     int H, int N, int Nk, int d, int causal, int n_qtiles, float c) {
-    constexpr int NCH = DMAX / 16;    // 4-float pieces per lane
+    constexpr int kRows = kThreads / LPR;   // query rows per workgroup
+    constexpr int NCH = DMAX / (4 * LPR);   // 4-float pieces per lane
+    static_assert(NCH >= 1 && NCH * 4 * LPR == DMAX, "width/lane split");
     __shared__ __attribute__((aligned(16))) float Ks[kBc * DMAX];
     __shared__ __attribute__((aligned(16))) float Vs[kBc * DMAX];
 
-    const int tid = threadIdx.x, part = tid & 3;
+    const int tid = threadIdx.x, part = tid % LPR;
     const int qtile = blockIdx.x % n_qtiles, bh = blockIdx.x / n_qtiles, b = bh / H;
-    const int qrow = qtile * kRows + (tid >> 2);
+    const int qrow = qtile * kRows + tid / LPR;
     const int off = Nk - N;
     const int kv_lim = visible_len(key_lens, b, Nk);
     int kv_end = kv_lim;
@@ -43,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     for (int k = 0; k < NCH; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int col = 16 * k + 4 * part + e;
+            const int col = 4 * LPR * k + 4 * part + e;
             q[k][e] = (qrow < N && col < d) ? Q[q_base + (size_t)qrow * d + col] : 0.f;
             o[k][e] = 0.f;
         }
@@ -85,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) kv[u][k] = *(const f32x4_t *)&Ks[(jg + u) * DMAX + 16 * k + 4 * part];
+                for (int k = 0; k < NCH; ++k) kv[u][k] = *(const f32x4_t *)&Ks[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
 #pragma unroll
             for (int u = 0; u < KG; ++u) {
                 float part_dot = 0.f;
@@ -93,8 +109,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
                 for (int k = 0; k < NCH; ++k)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) part_dot = fmaf(q[k][e], kv[u][k][e], part_dot);
-                part_dot += quad_xor_f32<1>(part_dot);
-                part_dot += quad_xor_f32<2>(part_dot);
+                part_dot = row_group_sum<LPR>(part_dot);
                 const int key = j0 + jg + u;
                 const bool ok = key < kv_lim && (!causal || key <= qrow + off);
                 s[jg + u] = ok ? part_dot : neg_inf();
@@ -118,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) vv[u][k] = *(const f32x4_t *)&Vs[(jg + u) * DMAX + 16 * k + 4 * part];
+                for (int k = 0; k < NCH; ++k) vv[u][k] = *(const f32x4_t *)&Vs[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
 #pragma unroll
             for (int u = 0; u < KG; ++u) {
                 const float p = exp2_hw(fmaf(s[jg + u], c, -ms_ref));
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
         for (int k = 0; k < NCH; ++k)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int col = 16 * k + 4 * part + e;
+                const int col = 4 * LPR * k + 4 * part + e;
                 if (col < d) O[q_base + (size_t)qrow * d + col] = o[k][e] * inv;
             }
         if (part == 0)
@@ -145,11 +160,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     }
 }
 
-template <int DMAX>
+template <int DMAX, int LPR>
 hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
+    constexpr int kRows = kThreads / LPR;
     const int n_qtiles = (a.N + kRows - 1) / kRows;
     const long long nblocks = (long long)a.B * a.H * n_qtiles;
-    hipLaunchKernelGGL(fwd_f32_kernel<DMAX>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_f32_kernel<DMAX, LPR>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        (const float *)a.Q, (const float *)a.K, (const float *)a.V, (float *)a.O,
                        a.LSE, a.key_lens, a.H, a.N, a.Nk, a.d, a.causal, n_qtiles,
                        a.scale * kLog2e);
@@ -159,10 +175,13 @@ hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream) {
-    if (a.d <= 16) return launch_one<16>(a, stream);
-    if (a.d <= 64) return launch_one<64>(a, stream);
-    if (a.d <= 128) return launch_one<128>(a, stream);
-    return launch_one<256>(a, stream);
+    // fewer 64-row workgroups than CUs (half as many for d > 128): 16 lanes per
+    // row instead of 4 (measured: 2-3x on such grids, slower beyond them)
+    const long long blocks4 = (long long)a.B * a.H * ((a.N + 63) / 64);
+    if (a.d <= 16) return launch_one<16, 4>(a, stream);
+    if (a.d <= 64) return blocks4 < 256 ? launch_one<64, 16>(a, stream) : launch_one<64, 4>(a, stream);
+    if (a.d <= 128) return blocks4 < 256 ? launch_one<128, 16>(a, stream) : launch_one<128, 4>(a, stream);
+    return blocks4 < 128 ? launch_one<256, 16>(a, stream) : launch_one<256, 4>(a, stream);
 }
 
 }  // namespace fa

@@ -46,6 +46,16 @@ def test_f32_head_dims_ragged(d, causal):
     forward_and_check(inp, causal, what="f32 ragged")
 
 
+@pytest.mark.parametrize("d", [64, 100, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_large_grid(d, causal):
+    # 2 x 32 heads of 256 rows: enough 64-row workgroups for the 4-lanes-per-row
+    # kernel (small grids take the 16-lane one); sampled rows of 8 heads
+    inp = random_case(2, 32, 256, 256, d, F32, seed=d + 7, device=DEV, key_lens=[256, 201])
+    rows = sample_rows(2, 32, 256, per_head=8, seed=d, bh_limit=8)
+    forward_and_check(inp, causal, what="f32 large grid", rows=rows)
+
+
 def test_f32_key_lens_edges():
     inp = random_case(5, 1, 40, 33, 32, F32, seed=9, device=DEV, key_lens=[0, 1, 32, 33, 1000])
     forward_and_check(inp, False, what="f32 key_lens")
