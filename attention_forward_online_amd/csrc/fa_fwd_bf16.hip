@@ -51,10 +51,19 @@
 //     d = 128 without spills.  K runs two tiles ahead, V one: iteration t
 //     loads K(t+2) into the stage K(t) left and V(t+1) into the stage V(t-1)
 //     left, and they land before the iteration's only barrier.
+//   * Small non-causal grids (at most one query block per CU): each block's
+//     key tiles are split in two halves run by two groups of four waves in
+//     one workgroup, each with its own LDS stages and its own (m, l, o); at
+//     the end group 1 hands its state to group 0 through LDS and group 0
+//     merges the two with the (m, l) merge ('Online Softmax & FlashAttention',
+//     Step 1) before the epilogue.  Blocks without any visible key write
+//     O = 0, LSE = -inf and leave at once.
 //   * Work order: one query block per workgroup, causal launches start with
 //     the longest blocks; all blocks of a head run on one XCD (the dispatcher
 //     deals workgroup ids to the 8 XCDs round-robin), so K/V re-reads of a
 //     head hit one L2, and consecutive heads go to different XCDs.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -78,9 +87,11 @@ constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs
 
 template <int N_> struct IntC { static constexpr int value = N_; };
 
-// d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
+// d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.  KSPLIT = 2
+// (non-causal only): two groups of four waves share each query block, group g
+// taking the g-th half of its key tiles; their states are merged at the end.
+template <int D, bool CAUSAL, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
@@ -99,21 +110,24 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     // choice neutral)
     constexpr int kPrioPhase = D == 64 ? 2 : 1;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && !CAUSAL), "key split: non-causal only");
 
     // one array per stage, so that the stage a load fills and the stage the
-    // MFMAs read are distinct objects
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBc * KS], Ks1[kBc * KS];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBc * VS], Vs1[kBc * VS];
+    // MFMAs read are distinct objects (with a key split: one half per group)
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KSPLIT * kBc * KS], Ks1[KSPLIT * kBc * KS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KSPLIT * kBc * VS], Vs1[KSPLIT * kBc * VS];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave >= 0 && wave < kWaves);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave_id >= 0 && wave_id < kWaves * KSPLIT);
+    const int grp = wave_id >> 2;               // key-split group
+    const int wave = wave_id & (kWaves - 1);    // wave within the group: its 32 query rows
     const int li = lane & 31, g = lane >> 5;
     const int krow = perm32(li);
     const int vrow = (li & 15) >> 2;
     const int vcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    auto kst = [&](int stage) -> uint16_t * { return stage ? Ks1 : Ks0; };
-    auto vst = [&](int stage) -> uint16_t * { return stage ? Vs1 : Vs0; };
+    auto kst = [&](int stage) -> uint16_t * { return (stage ? Ks1 : Ks0) + grp * (kBc * KS); };
+    auto vst = [&](int stage) -> uint16_t * { return (stage ? Vs1 : Vs0) + grp * (kBc * VS); };
 
     // workgroup -> (head, query block).  With B*H divisible by 8, head bh lives on
     // XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs round-robin):
@@ -145,11 +159,27 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     const int wq_first = q0 + wave * kRowsPerWave;
     const int wq_last = min(wq_first + kRowsPerWave, N) - 1;
     const int qrow = wq_first + li;
-    // tiles this wave sees: a prefix of the workgroup's tiles
+    if (ntiles == 0) {      // no visible key in the block: O = 0, LSE = -inf
+        if (grp == 0 && qrow < N) {
+            uint16_t *orow = O + q_base + (size_t)qrow * D;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j)
+                *(u32x4_t *)(orow + 16 * j + 8 * g) = u32x4_t{0u, 0u, 0u, 0u};
+            if (g == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+        }
+        return;
+    }
+    // the group's key tiles: tiles tbase .. tbase + ntg - 1 of the block; both
+    // groups pass nloop barriers in the tile loop
+    const int half = (ntiles + KSPLIT - 1) / KSPLIT;
+    const int tbase = grp * half;
+    const int ntg = KSPLIT == 1 ? ntiles : (grp ? ntiles - half : half);
+    const int nloop = half;
+    // tiles this wave sees: a prefix of its group's tiles
     int nt_w = 0;
     if (wq_first <= wq_last) {
         const int last_key = wq_last + off;
-        nt_w = !CAUSAL ? ntiles : (last_key < 0 ? 0 : min(ntiles, last_key / kBc + 1));
+        nt_w = !CAUSAL ? ntg : (last_key < 0 ? 0 : min(ntiles, last_key / kBc + 1));
     }
 
     u32x4_t qf[KK];
@@ -197,7 +227,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     window_offsets(IntC<VS>{}, goffv);
     auto dma = [&](auto nj_c, const uint32_t *goff, const uint16_t *src, uint16_t *dst, int t) {
         constexpr int NJ = decltype(nj_c)::value, MJ = (NJ + kWaves - 1) / kWaves;
-        const int j0 = t * kBc;
+        const int j0 = (tbase + t) * kBc;
         const rsrc_t r = make_rsrc(src + (size_t)j0 * D, (uint32_t)max(kv_end - j0, 0) * D * 2);
 #pragma unroll
         for (int m = 0; m < MJ; ++m)
@@ -238,11 +268,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
                      fmaxf(fmaxf(x[v0 + 3], x[v0 + 4]), fmaxf(fmaxf(x[v0 + 5], x[v0 + 6]), x[v0 + 7])));
     };
     auto need_mask = [&](int t) {
-        const int j0 = t * kBc;
+        const int j0 = (tbase + t) * kBc;
         return (j0 + kBc > kv_lim) || (CAUSAL && j0 + kBc - 1 > wq_first + off);
     };
     auto apply_mask = [&](int t, f32x16_t (&sc)[2]) {
-        const int j0 = t * kBc;
+        const int j0 = (tbase + t) * kBc;
         const int vis_end = CAUSAL ? min(kv_lim, qrow + off + 1) : kv_lim;
         const int lim = vis_end - j0 - 8 * g;
 #pragma unroll
@@ -272,9 +302,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     // prologue: K(0), V(0), K(1) into LDS, issued with the Q loads; S(0) is
     // prepared as soon as Q and K(0) have landed (every wave has at most its
     // V(0) and K(1) windows outstanding), the rest arrives meanwhile
-    dma_k(Ks0, 0);
-    dma_v(Vs0, 0);
-    dma_k(Ks1, 1);
+    dma_k(kst(0), 0);
+    dma_v(vst(0), 0);
+    dma_k(kst(1), 1);
     wait_vmem_le<NJV / kWaves + NJK / kWaves>();
     // every wave's K(0) windows are in LDS; the barrier carries no release
     // fence (that would wait for V(0) and K(1) too), the acquire fence keeps
@@ -362,10 +392,44 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
         step(IntC<0>{}, t, sa, sb);
         ++t;
     }
-    for (; t < ntiles; ++t) {
+    for (; t < nloop; ++t) {
         refill(t & 1, t);
         wait_vmem_all();
         __syncthreads();
+    }
+    if constexpr (KSPLIT == 2) {
+        // group 1 hands its (reference, l, o) to group 0 through the V stages
+        // (every wave is past its last LDS read and no load is in flight): one
+        // 256-byte row per register, lane-indexed
+        constexpr int RW = 16 * CB + 2;                      // rows per wave
+        constexpr int R0 = (int)(sizeof(Vs0) / 256);         // rows in Vs0
+        static_assert(kWaves * RW <= 2 * R0, "merge rows do not fit the V stages");
+        auto mrow = [&](int k) -> float * {
+            const int r = wave * RW + k;
+            return (r < R0 ? (float *)Vs0 + 64 * r : (float *)Vs1 + 64 * (r - R0)) + lane;
+        };
+        if (grp == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) *mrow(16 * cb + v) = acc[cb][v];
+            *mrow(16 * CB) = ms;
+            *mrow(16 * CB + 1) = l;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        // merge ('Online Softmax & FlashAttention', Step 1): common reference
+        // m = max(m0, m1), each side scaled by 2^(m_g - m), 0 for a side without keys
+        const float ms1 = *mrow(16 * CB), l1 = *mrow(16 * CB + 1);
+        const float mm = fmaxf(ms, ms1);
+        const float a0 = ms == neg_inf() ? 0.f : exp2_hw(ms - mm);
+        const float a1 = ms1 == neg_inf() ? 0.f : exp2_hw(ms1 - mm);
+        l = a0 * l + a1 * l1;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[cb][v] = a0 * acc[cb][v] + a1 * *mrow(16 * cb + v);
+        ms = mm;
     }
 
     // epilogue: O = o / l (0 for a row without keys), LSE = ms + log2 l in nats (-inf then)
@@ -387,24 +451,54 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void fwd_bf16_kernel(
     }
 }
 
+// CUs of the current device, looked up once per device
+int cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+template <int D, bool CAUSAL, int KSPLIT>
+hipError_t launch_one(const FwdArgs &a, int n_qtiles, long long nblocks, int xcd_interleave,
+                      hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, KSPLIT>), dim3((unsigned)nblocks),
+                       dim3(kThreads * KSPLIT), 0, stream, (const uint16_t *)a.Q,
+                       (const uint16_t *)a.K, (const uint16_t *)a.V, (uint16_t *)a.O, a.LSE,
+                       a.key_lens, a.H, a.N, a.Nk, n_qtiles, xcd_interleave, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
-hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
+hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
     const long long BH = (long long)a.B * a.H;
     const long long nblocks = BH * n_qtiles;
     const int xcd_interleave = (BH % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblocks), dim3(kThreads), 0,
-                       stream, (const uint16_t *)a.Q, (const uint16_t *)a.K,
-                       (const uint16_t *)a.V, (uint16_t *)a.O, a.LSE, a.key_lens, a.H, a.N,
-                       a.Nk, n_qtiles, xcd_interleave, a.scale * kLog2e);
-    return hipGetLastError();
+    // a non-causal grid of at most one block per CU leaves each CU with one
+    // four-wave workgroup (one wave per SIMD): split every block's keys over
+    // two groups of four waves instead.  Such a workgroup needs the LDS of two
+    // and runs one per CU, so with more blocks than CUs it would take more
+    // dispatch rounds than the unsplit grid (measured slower at 512 blocks).
+    if constexpr (!CAUSAL) {
+        if (nblocks <= cu_count())
+            return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, xcd_interleave, stream);
+    }
+    return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, xcd_interleave, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
-    if (a.d == 64) return a.causal ? launch_one<64, true>(a, stream) : launch_one<64, false>(a, stream);
-    return a.causal ? launch_one<128, true>(a, stream) : launch_one<128, false>(a, stream);
+    if (a.d == 64) return a.causal ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
+    return a.causal ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
 }
 
 }  // namespace fa

@@ -83,6 +83,23 @@ def test_bf16_key_lens(d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("extra_heads", [0, 1])
+def test_bf16_key_split_grid_boundary(d, extra_heads):
+    # a non-causal grid of at most one query block per CU runs each block's keys in
+    # two halves merged at the end; one more head per batch puts the same inputs on the
+    # unsplit path.  Key lengths: none (the block leaves at once), one tile split 1 / 0,
+    # tile edges, odd tile counts, full.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, N, Nk = 8, 100, 300
+    H = cus // B + extra_heads
+    kl = [0, 1, 64, 65, 129, 200, 255, 300]
+    inp = random_case(B, H, N, Nk, d, BF16, seed=41 + d, device=DEV, key_lens=kl)
+    rows = sample_rows(B, H, N, per_head=8, seed=d, bh_limit=40)
+    rows += [b * H * N + i for b in range(B) for i in (0, N - 1)]
+    forward_and_check(inp, False, what=f"bf16 {B * H} blocks vs {cus} CUs", rows=sorted(set(rows)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("sigma", [3.0, 12.0])
 def test_bf16_high_dynamic_range(d, sigma):
     inp = random_case(2, 4, 256, 640, d, BF16, seed=17, device=DEV, q_sigma=sigma, key_lens=[640, 333])
