@@ -156,7 +156,7 @@ def main():
     avg_launch = ms_step
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (avg_launch * 1e-3) / 1e12
-    traffic = measured_traffic("fwd_bf16_kernel<64,true>/" + HEADLINE)
+    traffic = measured_traffic("fwd_bf16_kernel<64,true,1>/" + HEADLINE)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -175,7 +175,7 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64,true>",
+                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64,true,1>",
                      "avg_launch_ms": round(avg_launch, 5)},
     }
     head_out = (o, lse)
