@@ -103,8 +103,19 @@ def _check_dev(name: str, t: torch.Tensor, dtype=None):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
-def _stream_handle(stream) -> Optional[int]:
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _same_device(*tensors) -> torch.device:
+    """The one GPU all given tensors (None skipped) live on; raises otherwise."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def _stream_handle(stream, dev: torch.device) -> Optional[int]:
+    """Handle of `stream` (default: torch's current stream of `dev`), which must be on `dev`."""
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if s.device != dev:
+        raise ValueError(f"stream is on {s.device}, the tensors on {dev}")
     return s.cuda_stream
 
 
@@ -130,9 +141,11 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
             raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
-    st = lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
-                        float(scale), int(bool(causal)), _ptr(key_lens), _dtype_code(q),
-                        _stream_handle(stream))
+    dev = _same_device(q, k, v, o, lse, key_lens)
+    with torch.cuda.device(dev):
+        st = lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
+                            float(scale), int(bool(causal)), _ptr(key_lens), _dtype_code(q),
+                            _stream_handle(stream, dev))
     if st != FA_OK:
         raise FaError(st, "fa_forward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -167,9 +180,11 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.fa_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d,
-                               float(scale), _ptr(key_lens), int(num_splits), _ptr(workspace),
-                               ws_bytes, _dtype_code(q), _stream_handle(stream))
+    dev = _same_device(q, k, v, o, lse, key_lens, workspace)
+    with torch.cuda.device(dev):
+        st = lib.fa_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d,
+                                   float(scale), _ptr(key_lens), int(num_splits), _ptr(workspace),
+                                   ws_bytes, _dtype_code(q), _stream_handle(stream, dev))
     if st != FA_OK:
         raise FaError(st, "fa_decode_splitkv",
                       lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
@@ -205,8 +220,10 @@ def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
     if workspace is not None:
         _check_dev("workspace", workspace)
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.fa_softmax(_ptr(x), _ptr(y), _ptr(lse), rows, cols, _dtype_code(x), _ptr(workspace),
-                        ws_bytes, _stream_handle(stream))
+    dev = _same_device(x, y, lse, workspace)
+    with torch.cuda.device(dev):
+        st = lib.fa_softmax(_ptr(x), _ptr(y), _ptr(lse), rows, cols, _dtype_code(x),
+                            _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
     if st != FA_OK:
         raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -231,10 +248,12 @@ def fa_forward_v1(q, k, v, o, lse, workspace, scale=None, causal=False, key_lens
         _check_dev("key_lens", key_lens, torch.int32)
     if scale is None:
         scale = 1.0 / (d ** 0.5)
-    st = lib.fa_forward_v1(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
-                           float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _dtype_code(q),
-                           _stream_handle(stream))
+    dev = _same_device(q, k, v, o, lse, key_lens, workspace)
+    with torch.cuda.device(dev):
+        st = lib.fa_forward_v1(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
+                               float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _dtype_code(q),
+                               _stream_handle(stream, dev))
     if st != FA_OK:
         raise FaError(st, "fa_forward_v1", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -281,9 +300,12 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=F
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                         _ptr(dv), B, H, N, Nk, d, float(scale), int(bool(causal)), _ptr(key_lens),
-                         _ptr(workspace), ws_bytes, _dtype_code(q), _stream_handle(stream))
+    dev = _same_device(q, k, v, o, do, lse, dq, dk, dv, key_lens, workspace)
+    with torch.cuda.device(dev):
+        st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), B, H, N, Nk, d, float(scale), int(bool(causal)),
+                             _ptr(key_lens), _ptr(workspace), ws_bytes, _dtype_code(q),
+                             _stream_handle(stream, dev))
     if st != FA_OK:
         raise FaError(st, "fa_backward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
