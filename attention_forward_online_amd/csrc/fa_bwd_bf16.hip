@@ -150,12 +150,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const float lse = LSE[(size_t)bh * N + qrow];
         l2 = lse == neg_inf() ? 0.f : lse * kLog2e;
     }
-    // D and LSE2 of the rows, for the dK/dV kernel that runs next, in per-head
-    // arrays of Npad = N rounded up to the 64-query tile; the padding gets
-    // zeros (its queries are masked there)
+    // LSE2 and -D of the rows, for the dK/dV kernel that runs next (it starts
+    // its dP accumulators at -D), in per-head arrays of Npad = N rounded up to
+    // the 64-query tile; the padding gets zeros (its queries are masked there)
     if (g == 0 && qrow < Npad) {
         L2[(size_t)bh * Npad + qrow] = qrow < N ? l2 : 0.f;
-        Dd[(size_t)bh * Npad + qrow] = qrow < N ? dd : 0.f;
+        Dd[(size_t)bh * Npad + qrow] = qrow < N ? -dd : 0.f;
     }
     wait_vmem_all();
 
@@ -462,23 +462,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                     if (!key_vis || i >= N || (CAUSAL && key > i + off)) s[qb][v] = neg_inf();
                 }
             };
-            // LSE2 and D of the 16 queries block qb gives this lane
-            f32x4_t lv[4], dv[4];
-            auto load_ld = [&](int qb) {
+            // LSE2 of the 16 queries block qb gives this lane, and their -D as
+            // the starting value of the block's dP accumulator (register order)
+            f32x4_t lv[4];
+            auto load_l = [&](int qb) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int i8 = 32 * qb + 16 * h + 8 * g;
                     lv[2 * h] = *(const f32x4_t *)&LDc[i8];
                     lv[2 * h + 1] = *(const f32x4_t *)&LDc[i8 + 4];
-                    dv[2 * h] = *(const f32x4_t *)&LDc[kTile + i8];
-                    dv[2 * h + 1] = *(const f32x4_t *)&LDc[kTile + i8 + 4];
                 }
+            };
+            auto minus_d = [&](int qb) {
+                f32x16_t x;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i8 = 32 * qb + 16 * h + 8 * g;
+                    const f32x4_t a = *(const f32x4_t *)&LDc[kTile + i8];
+                    const f32x4_t b = *(const f32x4_t *)&LDc[kTile + i8 + 4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[8 * h + e] = a[e];
+                        x[8 * h + 4 + e] = b[e];
+                    }
+                }
+                return x;
             };
             // P (and dS) of queries 2e, 2e + 1 of block qb as bf16 pairs
             auto p_pair = [&](int qb, int e) {
                 const int v = 2 * e;
                 const float l0 = lv[e >> 1][v & 3], l1 = lv[e >> 1][(v & 3) + 1];
-                const float d0 = dv[e >> 1][v & 3], d1 = dv[e >> 1][(v & 3) + 1];
                 const float p0 = exp2_hw(fmaf(s[qb][v], c, -l0));
                 const float p1 = exp2_hw(fmaf(s[qb][v + 1], c, -l1));
                 if constexpr (WANT_DV) {
@@ -486,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                     pin(pp[qb][e]);
                 }
                 if constexpr (WANT_DK) {
-                    pd[qb][e] = pack_bf16x2(p0 * (dp[qb][v] - d0), p1 * (dp[qb][v + 1] - d1));
+                    pd[qb][e] = pack_bf16x2(p0 * dp[qb][v], p1 * dp[qb][v + 1]);   // dP - D
                     pin(pd[qb][e]);
                 }
             };
@@ -501,20 +514,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                                      adk[cb]);
             };
             rows_block(Qc, kf, 0, s[0]);
-            if constexpr (WANT_DK) rows_block(Gc, vf, 0, dp[0]);
+            if constexpr (WANT_DK) {
+                dp[0] = minus_d(0);
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) dp[0] = mfma32(row_operand(Gc, 0, kk), vf[kk], dp[0]);
+            }
             if (need_mask) mask_block(0);
-            load_ld(0);
+            load_l(0);
+            if constexpr (WANT_DK) dp[1] = minus_d(1);
             // S (and dP) MFMAs of block 1, two P pairs of block 0 per S step
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 s[1] = mfma32(row_operand(Qc, 1, kk), kf[kk], kk == 0 ? f32x16_t{} : s[1]);
-                if constexpr (WANT_DK) dp[1] = mfma32(row_operand(Gc, 1, kk), vf[kk], kk == 0 ? f32x16_t{} : dp[1]);
+                if constexpr (WANT_DK) dp[1] = mfma32(row_operand(Gc, 1, kk), vf[kk], dp[1]);
 #pragma unroll
                 for (int e = 8 * kk / KK; e < 8 * (kk + 1) / KK; ++e) p_pair(0, e);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (need_mask) mask_block(1);
-            load_ld(1);
+            load_l(1);
             // dV, dK MFMAs of block 0 beside the P pairs of block 1
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
