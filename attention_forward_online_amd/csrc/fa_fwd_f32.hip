@@ -6,9 +6,12 @@
 // touches the data.  LPR lanes share a query row and split its d dimension in
 // 4-float pieces, so a score is LPR partial dot products combined by lane
 // exchanges (DPP) inside the row's lane group; a workgroup of 256 threads holds
-// 256 / LPR rows.  LPR = 4 in general; small grids (a few workgroups, e.g. one
-// 256-row head) take LPR = 16, which gives four times the waves and a quarter
-// of the per-lane work per key.  K/V tiles of 32 keys are staged in LDS,
+// 256 / LPR rows.  LPR = 4 in general; small grids take LPR = 16, which gives
+// four times the waves and a quarter of the per-lane work per key, and the
+// smallest (fewer 16-row blocks than CUs, e.g. one 256-row head) also split
+// each block's keys over its four waves (4 rows per workgroup, key tiles
+// dealt round-robin to the waves, states merged at the end), which shortens
+// the serial key loop of every row four times.  K/V tiles of 32 keys are staged in LDS,
 // zero-padded to the compiled width DMAX (zeros add nothing to a dot product
 // and the padded output columns are never stored).
 // Fully masked rows give O = 0 and LSE = -inf as in the bf16 path.
@@ -33,20 +36,27 @@ __device__ __forceinline__ float row_group_sum(float x) {
     return x;
 }
 
-template <int DMAX, int LPR>
+// KW > 1 (small grids): the workgroup's threads form KW "ways" of kThreads / KW
+// lanes over the same rows; way w takes the key tiles w, w + KW, w + 2 KW, ...
+// with its own LDS tile, and the ways' states are merged at the end.
+template <int DMAX, int LPR, int KW>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ key_lens,
     int H, int N, int Nk, int d, int causal, int n_qtiles, float c) {
-    constexpr int kRows = kThreads / LPR;   // query rows per workgroup
+    constexpr int TW = kThreads / KW;       // threads per way
+    constexpr int kRows = TW / LPR;         // query rows per workgroup
     constexpr int NCH = DMAX / (4 * LPR);   // 4-float pieces per lane
     static_assert(NCH >= 1 && NCH * 4 * LPR == DMAX, "width/lane split");
-    __shared__ __attribute__((aligned(16))) float Ks[kBc * DMAX];
-    __shared__ __attribute__((aligned(16))) float Vs[kBc * DMAX];
+    static_assert(KW == 1 || TW % 64 == 0, "a way is whole waves");
+    __shared__ __attribute__((aligned(16))) float Ks[KW * kBc * DMAX];
+    __shared__ __attribute__((aligned(16))) float Vs[KW * kBc * DMAX];
 
-    const int tid = threadIdx.x, part = tid % LPR;
+    const int tid = threadIdx.x, way = tid / TW, wtid = tid % TW, part = wtid % LPR;
     const int qtile = blockIdx.x % n_qtiles, bh = blockIdx.x / n_qtiles, b = bh / H;
-    const int qrow = qtile * kRows + tid / LPR;
+    const int qrow = qtile * kRows + wtid / LPR;
+    float *const Kw = Ks + way * (kBc * DMAX);
+    float *const Vw = Vs + way * (kBc * DMAX);
     const int off = Nk - N;
     const int kv_lim = visible_len(key_lens, b, Nk);
     int kv_end = kv_lim;
@@ -71,24 +81,31 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     constexpr bool kPrefetch = DMAX <= 64;
     const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
     const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)max(kv_end, 0) * d * 4);
-    F32TileStage<kBc, DMAX, kThreads> kst, vst;
-    if (kPrefetch && ntiles > 0) {
-        kst.load(ksrc, 0, d, tid);
-        vst.load(vsrc, 0, d, tid);
+    F32TileStage<kBc, DMAX, TW> kst, vst;
+    if (kPrefetch && way < ntiles) {
+        kst.load(ksrc, way * kBc, d, wtid);
+        vst.load(vsrc, way * kBc, d, wtid);
     }
-    for (int t = 0; t < ntiles; ++t) {
+    // every way runs the same number of iterations (one barrier pair each);
+    // a way past its last tile only joins the barriers
+    const int nit = (ntiles + KW - 1) / KW;
+    for (int it = 0; it < nit; ++it) {
+        const int t = it * KW + way;
         const int j0 = t * kBc;
-        if (!kPrefetch) {
-            kst.load(ksrc, j0, d, tid);
-            vst.load(vsrc, j0, d, tid);
+        if (!kPrefetch && t < ntiles) {
+            kst.load(ksrc, j0, d, wtid);
+            vst.load(vsrc, j0, d, wtid);
         }
         __syncthreads();   // previous tile fully consumed
-        kst.store(Ks, tid);
-        vst.store(Vs, tid);
+        if (t < ntiles) {
+            kst.store(Kw, wtid);
+            vst.store(Vw, wtid);
+        }
         __syncthreads();
-        if (kPrefetch && t + 1 < ntiles) {
-            kst.load(ksrc, j0 + kBc, d, tid);
-            vst.load(vsrc, j0 + kBc, d, tid);
+        if (t >= ntiles) continue;
+        if (kPrefetch && t + KW < ntiles) {
+            kst.load(ksrc, j0 + KW * kBc, d, wtid);
+            vst.load(vsrc, j0 + KW * kBc, d, wtid);
         }
 
         // keys are taken in groups whose K rows are read from LDS in one batch
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) kv[u][k] = *(const f32x4_t *)&Ks[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
+                for (int k = 0; k < NCH; ++k) kv[u][k] = *(const f32x4_t *)&Kw[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
 #pragma unroll
             for (int u = 0; u < KG; ++u) {
                 float part_dot = 0.f;
@@ -133,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int u = 0; u < KG; ++u)
 #pragma unroll
-                for (int k = 0; k < NCH; ++k) vv[u][k] = *(const f32x4_t *)&Vs[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
+                for (int k = 0; k < NCH; ++k) vv[u][k] = *(const f32x4_t *)&Vw[(jg + u) * DMAX + 4 * LPR * k + 4 * part];
 #pragma unroll
             for (int u = 0; u < KG; ++u) {
                 const float p = exp2_hw(fmaf(s[jg + u], c, -ms_ref));
@@ -146,6 +163,39 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
         }
     }
 
+    if constexpr (KW > 1) {
+        // ways 1.. hand (ms, l, o) to way 0 through LDS (per lane, 2 + 4 NCH
+        // floats); way 0 merges them in way order with the (m, l) merge
+        // ('Online Softmax & FlashAttention', Step 1)
+        constexpr int NV = 2 + 4 * NCH;
+        static_assert((KW - 1) * TW * NV <= KW * kBc * DMAX, "merge state does not fit");
+        __syncthreads();   // every way is past its last LDS read
+        if (way > 0) {
+            float *st = Ks + ((way - 1) * NV) * TW + wtid;
+            st[0] = ms;
+            st[TW] = l;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[(2 + 4 * k + e) * TW] = o[k][e];
+        }
+        __syncthreads();
+        if (way > 0) return;
+#pragma unroll
+        for (int w = 1; w < KW; ++w) {
+            const float *st = Ks + ((w - 1) * NV) * TW + wtid;
+            const float ms2 = st[0], l2 = st[TW];
+            const float mm = fmaxf(ms, ms2);
+            const float a1 = ms == neg_inf() ? 0.f : exp2_hw(ms - mm);
+            const float a2 = ms2 == neg_inf() ? 0.f : exp2_hw(ms2 - mm);
+            l = a1 * l + a2 * l2;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[k][e] = a1 * o[k][e] + a2 * st[(2 + 4 * k + e) * TW];
+            ms = mm;
+        }
+    }
     if (qrow < N) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -160,12 +210,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
     }
 }
 
-template <int DMAX, int LPR>
+template <int DMAX, int LPR, int KW = 1>
 hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
-    constexpr int kRows = kThreads / LPR;
+    constexpr int kRows = kThreads / KW / LPR;
     const int n_qtiles = (a.N + kRows - 1) / kRows;
     const long long nblocks = (long long)a.B * a.H * n_qtiles;
-    hipLaunchKernelGGL((fwd_f32_kernel<DMAX, LPR>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_f32_kernel<DMAX, LPR, KW>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        (const float *)a.Q, (const float *)a.K, (const float *)a.V, (float *)a.O,
                        a.LSE, a.key_lens, a.H, a.N, a.Nk, a.d, a.causal, n_qtiles,
                        a.scale * kLog2e);
@@ -177,10 +227,20 @@ hipError_t launch_one(const FwdArgs &a, hipStream_t stream) {
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream) {
     // fewer 64-row workgroups than CUs (half as many for d > 128): 16 lanes per
     // row instead of 4 (measured: 2-3x on such grids, slower beyond them)
+    // fewer 16-row workgroups than that: 4-row workgroups whose four waves
+    // split the keys (four times the workgroups, a quarter of the serial key
+    // loop per wave)
     const long long blocks4 = (long long)a.B * a.H * ((a.N + 63) / 64);
+    const long long blocks16 = (long long)a.B * a.H * ((a.N + 15) / 16);
     if (a.d <= 16) return launch_one<16, 4>(a, stream);
-    if (a.d <= 64) return blocks4 < 256 ? launch_one<64, 16>(a, stream) : launch_one<64, 4>(a, stream);
-    if (a.d <= 128) return blocks4 < 256 ? launch_one<128, 16>(a, stream) : launch_one<128, 4>(a, stream);
+    if (a.d <= 64) {
+        if (blocks16 < 256) return launch_one<64, 16, 4>(a, stream);
+        return blocks4 < 256 ? launch_one<64, 16>(a, stream) : launch_one<64, 4>(a, stream);
+    }
+    if (a.d <= 128) {
+        if (blocks16 < 256) return launch_one<128, 16, 4>(a, stream);
+        return blocks4 < 256 ? launch_one<128, 16>(a, stream) : launch_one<128, 4>(a, stream);
+    }
     return blocks4 < 128 ? launch_one<256, 16>(a, stream) : launch_one<256, 4>(a, stream);
 }
 
