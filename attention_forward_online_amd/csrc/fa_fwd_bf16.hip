@@ -35,7 +35,8 @@
 //     v_exp_f32 per score; P is rounded to bf16 (RNE) only as the MFMA operand
 //     while the row sum uses the fp32 values.
 //   * Lazy rescale: the reference max moves only when a tile's max exceeds it
-//     by more than 2^8 (FA-4's thresholded rescale); o and l always share the
+//     by more than 8 in log2 units, i.e. a weight would pass 2^8 (FA-4's
+//     thresholded rescale); o and l always share the
 //     reference, so the result is unchanged while most tiles skip the
 //     rescale of the accumulators.
 //   * Software pipeline within each wave: iteration t issues the MFMAs of

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -72,12 +73,16 @@ def time_region(fn, steps, warmup):
 
 
 def kernel_source_hash():
+    """sha256 (first 16 hex digits) of the kernel sources with comments and
+    white space removed: any change to the code changes it, an edit to a
+    comment alone does not."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_forward_online_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", f.read(), flags=re.S)
+            h.update(name.encode() + "".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
