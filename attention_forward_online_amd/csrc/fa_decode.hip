@@ -105,7 +105,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float q[EPL];
     Elem<T>::widen(*(const u32x4_t *)(Q + bh * D + cl * EPL), q);
 
-    float ms = neg_inf(), l = 0.f, o[EPL];
+    // the running denominator is l + lc: each iteration's sum of weights is
+    // added with an error-free two-sum whose rounding error accumulates in lc
+    // (a chunk can hold millions of keys)
+    float ms = neg_inf(), l = 0.f, lc = 0.f, o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
@@ -138,18 +141,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         const float alpha = exp2_hw(ms - ref);
         ms = ms_new;
         l *= alpha;
+        lc *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+        float lt = 0.f;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const float p = exp2_hw(fmaf(s[u], c, -ref));
             float vf[EPL];
             Elem<T>::widen(vr[u], vf);
-            l += p;
+            lt += p;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
         }
+        const float ls = l + lt, bv = ls - l;
+        lc += (l - (ls - bv)) + (lt - bv);
+        l = ls;
     }
+    l += lc;
 
     // merge the RPW row groups of this wave (lanes with equal cl)
 #pragma unroll

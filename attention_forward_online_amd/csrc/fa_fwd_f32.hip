@@ -73,7 +73,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
             q[k][e] = (qrow < N && col < d) ? Q[q_base + (size_t)qrow * d + col] : 0.f;
             o[k][e] = 0.f;
         }
-    float ms = neg_inf(), l = 0.f;
+    // the running denominator is l + lc: each tile's sum of weights is added
+    // with an error-free two-sum whose rounding error accumulates in lc, so a
+    // row over millions of keys keeps fp32 accuracy in LSE
+    float ms = neg_inf(), l = 0.f, lc = 0.f;
 
     // K/V tiles: all of a thread's loads are issued at once, and (up to
     // DMAX = 64, where the registers allow it without losing a wave) the next
@@ -140,10 +143,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
         const float alpha = exp2_hw(ms - ms_ref);
         ms = ms_new;
         l *= alpha;
+        lc *= alpha;
 #pragma unroll
         for (int k = 0; k < NCH; ++k)
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[k][e] *= alpha;
+        float lt = 0.f;   // this tile's weights
 #pragma unroll
         for (int jg = 0; jg < kBc; jg += KG) {
             f32x4_t vv[KG][NCH];
@@ -154,14 +159,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 #pragma unroll
             for (int u = 0; u < KG; ++u) {
                 const float p = exp2_hw(fmaf(s[jg + u], c, -ms_ref));
-                l += p;
+                lt += p;
 #pragma unroll
                 for (int k = 0; k < NCH; ++k)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) o[k][e] = fmaf(p, vv[u][k][e], o[k][e]);
             }
         }
+        const float ls = l + lt, bv = ls - l;
+        lc += (l - (ls - bv)) + (lt - bv);
+        l = ls;
     }
+    l += lc;
 
     if constexpr (KW > 1) {
         // ways 1.. hand (ms, l, o) to way 0 through LDS (per lane, 2 + 4 NCH

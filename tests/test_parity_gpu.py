@@ -100,6 +100,25 @@ def test_bf16_key_split_grid_boundary(d, extra_heads):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_largest_slice(d, causal):
+    # the largest K/V slice per (batch, head) the library accepts: Nk * d * 2 bytes just
+    # under 2^31 (its 32-bit buffer offsets); a key more is rejected before any launch
+    Nk = ((1 << 31) - 256) // (2 * d)
+    N = 130
+    inp = random_case(1, 1, N, Nk, d, BF16, seed=7 + d, device=DEV)
+    rows = [0, 1, 63, 64, 127, 128, N - 1]
+    forward_and_check(inp, causal, what=f"bf16 largest slice Nk={Nk}", rows=rows)
+    k1 = torch.empty(1, 1, Nk + 1, d, dtype=BF16, device=DEV)
+    o = torch.empty_like(inp["q"])
+    lse = torch.empty(1, 1, N, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa.FaError, match="FA_ERR_INVALID_ARG"):
+        fa.fa_forward(inp["q"], k1, k1, o, lse, causal=causal)
+    del inp, k1
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("sigma", [3.0, 12.0])
 def test_bf16_high_dynamic_range(d, sigma):
     inp = random_case(2, 4, 256, 640, d, BF16, seed=17, device=DEV, q_sigma=sigma, key_lens=[640, 333])
@@ -211,6 +230,31 @@ def test_decode_matches_forward_and_split_invariance():
     o1, l1 = fa.decode(q, k, v, num_splits=16, key_lens=kl)
     torch.cuda.synchronize()
     assert torch.equal(o1, outs[3][0]) and torch.equal(l1, outs[3][1])
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_decode_largest_slice(dtype):
+    # the largest K/V slice per (batch, head) the decode accepts (Nk * d * element size
+    # just under 2^31), over 16 splits, with and without a key length cutting it
+    d = 128
+    esz = 4 if dtype == F32 else 2
+    Nk = ((1 << 31) - 256) // (esz * d)
+    inp = random_case(2, 1, 1, Nk, d, dtype, seed=3, device=DEV, key_lens=[Nk, Nk // 3 + 5])
+    _decode_check(inp, 16, f"decode largest slice Nk={Nk}")
+    _decode_check(inp, 1, f"decode largest slice Nk={Nk}, one split")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_f32_largest_slice():
+    # fp32 prefill at the largest accepted slice (Nk * d * 4 bytes just under 2^31)
+    d = 64
+    Nk = ((1 << 31) - 256) // (4 * d)
+    inp = random_case(1, 1, 37, Nk, d, F32, seed=5, device=DEV)
+    forward_and_check(inp, False, what=f"f32 largest slice Nk={Nk}", rows=[0, 1, 17, 36])
+    forward_and_check(inp, True, what=f"f32 largest slice causal Nk={Nk}", rows=[0, 1, 17, 36])
+    del inp
+    torch.cuda.empty_cache()
 
 
 def test_decode_workload_full_size_sampled():
