@@ -92,31 +92,45 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _check_dev(name: str, t: torch.Tensor, dtype=None):
+# raw handle of torch's current stream on a GPU (a private but stable torch
+# entry point; the public one builds a Stream object on every call)
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _check_dev(name: str, t, dtype=None, idx: Optional[int] = None) -> None:
+    """`t` must be a contiguous GPU tensor, of `dtype` and on GPU `idx` when given.
+    The passing case is one combined test; a message is built only on failure."""
+    if (isinstance(t, torch.Tensor) and t.is_cuda and (dtype is None or t.dtype == dtype)
+            and (idx is None or t.get_device() == idx) and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must live on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if idx is not None and t.get_device() != idx:
+        raise ValueError(f"{name} is on cuda:{t.get_device()}, the other tensors on cuda:{idx}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    raise ValueError(f"{name} must be contiguous")
 
 
-def _same_device(*tensors) -> torch.device:
-    """The one GPU all given tensors (None skipped) live on; raises otherwise."""
-    devs = {t.device for t in tensors if t is not None}
-    if len(devs) != 1:
-        raise ValueError(f"all tensors must be on one GPU, got {sorted(map(str, devs))}")
-    return devs.pop()
+def _launch(idx: int, stream, call):
+    """Run call(stream handle) with GPU `idx` current.  `stream` (default: torch's
+    current stream of that GPU) must belong to it."""
+    if stream is not None and stream.device_index != idx:
+        raise ValueError(f"stream is on cuda:{stream.device_index}, the tensors on cuda:{idx}")
 
+    def handle():
+        if stream is not None:
+            return stream.cuda_stream
+        if _raw_current_stream is not None:
+            return _raw_current_stream(idx)
+        return torch.cuda.current_stream(idx).cuda_stream
 
-def _stream_handle(stream, dev: torch.device) -> Optional[int]:
-    """Handle of `stream` (default: torch's current stream of `dev`), which must be on `dev`."""
-    s = stream if stream is not None else torch.cuda.current_stream(dev)
-    if s.device != dev:
-        raise ValueError(f"stream is on {s.device}, the tensors on {dev}")
-    return s.cuda_stream
+    if torch.cuda.current_device() == idx:
+        return call(handle())
+    with torch.cuda.device(idx):
+        return call(handle())
 
 
 def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -126,26 +140,26 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
 
     q, o: [B,H,N,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,N]; key_lens: int32 [B] or None.
     """
-    lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _check_dev(n, t, q.dtype)
-    _check_dev("lse", lse, torch.float32)
+    lib = _lib or load_library()
+    _check_dev("q", q)
+    idx = q.get_device()
+    for n, t in (("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype, idx)
+    _check_dev("lse", lse, torch.float32, idx)
     B, H, N, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
             or lse.shape != (B, H, N):
         raise ValueError("shape mismatch between q, k, v, o and lse")
     if key_lens is not None:
-        _check_dev("key_lens", key_lens, torch.int32)
+        _check_dev("key_lens", key_lens, torch.int32, idx)
         if key_lens.shape != (B,):
             raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
-    dev = _same_device(q, k, v, o, lse, key_lens)
-    with torch.cuda.device(dev):
-        st = lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
-                            float(scale), int(bool(causal)), _ptr(key_lens), _dtype_code(q),
-                            _stream_handle(stream, dev))
+    st = _launch(idx, stream, lambda h: lib.fa_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d, float(scale),
+        int(bool(causal)), _ptr(key_lens), _dtype_code(q), h))
     if st != FA_OK:
         raise FaError(st, "fa_forward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -163,28 +177,28 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     q, o: [B,H,1,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,1]; workspace: a GPU
     tensor of at least fa_decode_workspace_bytes(B, H, d, num_splits) bytes.
     """
-    lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _check_dev(n, t, q.dtype)
-    _check_dev("lse", lse, torch.float32)
-    _check_dev("workspace", workspace)
+    lib = _lib or load_library()
+    _check_dev("q", q)
+    idx = q.get_device()
+    for n, t in (("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype, idx)
+    _check_dev("lse", lse, torch.float32, idx)
+    _check_dev("workspace", workspace, None, idx)
     B, H, N, d = q.shape
     Nk = k.shape[2]
     if N != 1 or k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
             or lse.shape != (B, H, 1):
         raise ValueError("decode expects q, o [B,H,1,d], k, v [B,H,Nk,d], lse [B,H,1]")
     if key_lens is not None:
-        _check_dev("key_lens", key_lens, torch.int32)
+        _check_dev("key_lens", key_lens, torch.int32, idx)
         if key_lens.shape != (B,):
             raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
-    dev = _same_device(q, k, v, o, lse, key_lens, workspace)
-    with torch.cuda.device(dev):
-        st = lib.fa_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d,
-                                   float(scale), _ptr(key_lens), int(num_splits), _ptr(workspace),
-                                   ws_bytes, _dtype_code(q), _stream_handle(stream, dev))
+    st = _launch(idx, stream, lambda h: lib.fa_decode_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d, float(scale),
+        _ptr(key_lens), int(num_splits), _ptr(workspace), ws_bytes, _dtype_code(q), h))
     if st != FA_OK:
         raise FaError(st, "fa_decode_splitkv",
                       lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
@@ -204,26 +218,25 @@ def fa_softmax(x: torch.Tensor, y: Optional[torch.Tensor], lse: torch.Tensor,
     GPU tensor of at least fa_softmax_workspace_bytes(rows, cols, dtype) bytes
     (None when that is 0).
     """
-    lib = load_library()
+    lib = _lib or load_library()
     _check_dev("x", x)
+    idx = x.get_device()
     if x.dim() != 2:
         raise ValueError("x must be [rows, cols]")
     rows, cols = x.shape
     if y is not None:
-        _check_dev("y", y, x.dtype)
+        _check_dev("y", y, x.dtype, idx)
         if y.shape != x.shape:
             raise ValueError("y must have the shape of x")
-    _check_dev("lse", lse, torch.float32)
+    _check_dev("lse", lse, torch.float32, idx)
     if lse.shape != (rows,):
         raise ValueError("lse must have shape [rows]")
     ws_bytes = 0
     if workspace is not None:
-        _check_dev("workspace", workspace)
+        _check_dev("workspace", workspace, None, idx)
         ws_bytes = workspace.numel() * workspace.element_size()
-    dev = _same_device(x, y, lse, workspace)
-    with torch.cuda.device(dev):
-        st = lib.fa_softmax(_ptr(x), _ptr(y), _ptr(lse), rows, cols, _dtype_code(x),
-                            _ptr(workspace), ws_bytes, _stream_handle(stream, dev))
+    st = _launch(idx, stream, lambda h: lib.fa_softmax(
+        _ptr(x), _ptr(y), _ptr(lse), rows, cols, _dtype_code(x), _ptr(workspace), ws_bytes, h))
     if st != FA_OK:
         raise FaError(st, "fa_softmax", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -235,25 +248,27 @@ def fa_forward_v1_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 def fa_forward_v1(q, k, v, o, lse, workspace, scale=None, causal=False, key_lens=None,
                   stream=None) -> None:
     """The forward in the V1 loop order (ablation) through fa_forward_v1."""
-    lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        _check_dev(n, t, q.dtype)
-    _check_dev("lse", lse, torch.float32)
-    _check_dev("workspace", workspace)
+    lib = _lib or load_library()
+    _check_dev("q", q)
+    idx = q.get_device()
+    for n, t in (("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype, idx)
+    _check_dev("lse", lse, torch.float32, idx)
+    _check_dev("workspace", workspace, None, idx)
     B, H, N, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != k.shape or o.shape != q.shape or lse.shape != (B, H, N):
         raise ValueError("shape mismatch between q, k, v, o and lse")
     if key_lens is not None:
-        _check_dev("key_lens", key_lens, torch.int32)
+        _check_dev("key_lens", key_lens, torch.int32, idx)
+        if key_lens.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
-    dev = _same_device(q, k, v, o, lse, key_lens, workspace)
-    with torch.cuda.device(dev):
-        st = lib.fa_forward_v1(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d,
-                               float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _dtype_code(q),
-                               _stream_handle(stream, dev))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _launch(idx, stream, lambda h: lib.fa_forward_v1(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d, float(scale),
+        int(bool(causal)), _ptr(key_lens), _ptr(workspace), ws_bytes, _dtype_code(q), h))
     if st != FA_OK:
         raise FaError(st, "fa_forward_v1", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
@@ -281,12 +296,13 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=F
     [B,H,N] from fa_forward; workspace: a GPU tensor of at least
     fa_backward_workspace_bytes(B, H, N) bytes.
     """
-    lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
-                 ("dv", dv)):
-        _check_dev(n, t, q.dtype)
-    _check_dev("lse", lse, torch.float32)
-    _check_dev("workspace", workspace)
+    lib = _lib or load_library()
+    _check_dev("q", q)
+    idx = q.get_device()
+    for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_dev(n, t, q.dtype, idx)
+    _check_dev("lse", lse, torch.float32, idx)
+    _check_dev("workspace", workspace, None, idx)
     B, H, N, d = q.shape
     Nk = k.shape[2]
     if (k.shape != (B, H, Nk, d) or v.shape != k.shape or dk.shape != k.shape or dv.shape != k.shape
@@ -294,18 +310,16 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=F
             or lse.shape != (B, H, N)):
         raise ValueError("shape mismatch between q, k, v, o, do, lse and the gradients")
     if key_lens is not None:
-        _check_dev("key_lens", key_lens, torch.int32)
+        _check_dev("key_lens", key_lens, torch.int32, idx)
         if key_lens.shape != (B,):
             raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
-    dev = _same_device(q, k, v, o, do, lse, dq, dk, dv, key_lens, workspace)
-    with torch.cuda.device(dev):
-        st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                             _ptr(dk), _ptr(dv), B, H, N, Nk, d, float(scale), int(bool(causal)),
-                             _ptr(key_lens), _ptr(workspace), ws_bytes, _dtype_code(q),
-                             _stream_handle(stream, dev))
+    st = _launch(idx, stream, lambda h: lib.fa_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, Nk, d, float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
+        ws_bytes, _dtype_code(q), h))
     if st != FA_OK:
         raise FaError(st, "fa_backward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
