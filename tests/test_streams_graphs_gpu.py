@@ -77,25 +77,39 @@ def test_graph_replays_forward_and_decode():
     od = torch.empty_like(qd)
     ld = torch.empty((B, H, 1), device=DEV, dtype=torch.float32)
     ws = torch.empty(fa.fa_decode_workspace_bytes(B, H, d, 8) // 4, device=DEV, dtype=torch.float32)
-    for t in (q, k, v, qd):
+    # a non-causal call on this small grid runs the key-split kernel; key length 0
+    # for one batch takes the early exit
+    o2, lse2 = torch.empty_like(q), torch.empty_like(lse)
+    kl = torch.tensor([0, 201], dtype=torch.int32, device=DEV)
+    # a small fp32 call runs the key-ways fp32 kernel
+    qf = torch.empty((1, 2, 77, 64), device=DEV, dtype=torch.float32)
+    kf, vf, of = torch.empty_like(qf), torch.empty_like(qf), torch.empty_like(qf)
+    lf = torch.empty((1, 2, 77), device=DEV, dtype=torch.float32)
+    for t in (q, k, v, qd, qf, kf, vf):
         t.copy_(fresh(t.shape, t.dtype, 0))
 
     def step():
         fa.fa_forward(q, k, v, o, lse, causal=True)
         fa.fa_decode_splitkv(qd, k, v, od, ld, 8, ws)
+        fa.fa_forward(q, k, v, o2, lse2, causal=False, key_lens=kl)
+        fa.fa_forward(qf, kf, vf, of, lf, causal=False)
 
     graph = capture(step)
     for r in range(3):
         say(f"[gpu] graphs: forward + decode replay {r}")
-        for i, t in enumerate((q, k, v, qd)):
+        for i, t in enumerate((q, k, v, qd, qf, kf, vf)):
             t.copy_(fresh(t.shape, t.dtype, 10 * r + i + 1))
         graph.replay()
         torch.cuda.synchronize()
         oe, le = fa.attention(q, k, v, causal=True)
         ode, lde = fa.decode(qd, k, v, num_splits=8)
+        oe2, le2 = fa.attention(q, k, v, causal=False, key_lens=kl)
+        oef, lef = fa.attention(qf, kf, vf, causal=False)
         torch.cuda.synchronize()
         assert same(o, oe) and same(lse, le), f"replay {r}: forward differs from eager"
         assert same(od, ode) and same(ld, lde), f"replay {r}: decode differs from eager"
+        assert same(o2, oe2) and same(lse2, le2), f"replay {r}: key-split forward differs from eager"
+        assert same(of, oef) and same(lf, lef), f"replay {r}: fp32 forward differs from eager"
 
 
 @pytest.mark.parametrize("cols", [3000, 70001, 262144])
