@@ -1,0 +1,73 @@
+"""Host logic of bench.py (no GPU): the algorithmic FLOP and byte counts it
+divides by, the kernel-source hash that decides whether the committed counter
+runs still describe the kernels, and the refusal of more than one GPU."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from attention_forward_online_amd.synth import SOFTMAX_WORKLOADS, WORKLOADS  # noqa: E402
+
+
+def test_prefill_flops():
+    # 4 B H N Nk d (QK^T and PV, 2 FLOPs per multiply-add), halved for causal
+    w = WORKLOADS["causal_bf16_b4h16_n2048_d64"]
+    assert bench.prefill_flops(w) == 2 * 4 * 16 * 2048 * 2048 * 64
+    w = WORKLOADS["causal_bf16_b1h32_n8192_d128"]
+    assert bench.prefill_flops(w) == 2 * 32 * 8192 * 8192 * 128
+    w = WORKLOADS["tiny_f32_b1h1_n256_d64"]
+    assert bench.prefill_flops(w) == 4 * 256 * 256 * 64
+    # with key lengths only the visible keys count (clamped to [0, Nk])
+    w = WORKLOADS["masked_bf16_b2h8_n4096_d128"]
+    assert bench.prefill_flops(w, [1013, 0]) == 4 * 8 * 4096 * 128 * 1013
+    assert bench.prefill_flops(w, [-5, 10 ** 9]) == 4 * 8 * 4096 * 128 * 4096
+
+
+def test_decode_bytes():
+    # K and V read once, Q read, O and LSE written
+    w = WORKLOADS["decode_bf16_b64h32_nk16384_d128"]
+    kv = 2 * 64 * 32 * 16384 * 128 * 2
+    assert bench.decode_bytes(w) == kv + 2 * 64 * 32 * 128 * 2 + 64 * 32 * 4
+    assert bench.decode_bytes(w) == 17180925952
+
+
+def test_softmax_bytes():
+    w = next(iter(SOFTMAX_WORKLOADS.values()))
+    el = 2 if w.dtype == "bf16" else 4
+    assert bench.softmax_bytes(w) == 2 * w.rows * w.cols * el + w.rows * 4
+
+
+def _hash_of(tree, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tree))
+    return bench.kernel_source_hash()
+
+
+def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    csrc = tmp_path / "attention_forward_online_amd" / "csrc"
+    shutil.copytree(os.path.join(ROOT, "attention_forward_online_amd", "csrc"), csrc,
+                    ignore=shutil.ignore_patterns("*.o", "*.so"))
+    h0 = _hash_of(tmp_path, monkeypatch)
+    assert h0 == _hash_of(tmp_path, monkeypatch)          # deterministic
+    f = csrc / "fa_decode.hip"
+    text = f.read_text()
+    f.write_text("// an added line comment\n/* and a\n   block comment */\n" +
+                 text.replace("\n", "\n\n", 3))
+    assert _hash_of(tmp_path, monkeypatch) == h0          # comments, blank lines: same
+    f.write_text(text.replace("kUnroll = 16", "kUnroll = 8", 1))
+    assert "kUnroll = 16" in text
+    assert _hash_of(tmp_path, monkeypatch) != h0          # a code change: different
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
