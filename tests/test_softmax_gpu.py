@@ -256,3 +256,33 @@ def test_one_pass_wait_fallback(dtype):
     check_rows(to_host(x), y, lse, f"fallback {dtype}", dtype)
     y2, lse2 = run(x)
     check_rows(to_host(x), y2, lse2, f"after fallback {dtype}", dtype)
+
+
+# one-pass out-of-place rows hold at most 128 chunks of 64 KiB (16384 fp32 or
+# 32768 bf16 elements); one element more takes the two-pass kernels
+@pytest.mark.parametrize("dtype,chunk", [(torch.float32, 16384), (torch.bfloat16, 32768)])
+@pytest.mark.parametrize("extra", [0, 1])
+def test_rows_at_the_chunk_limit(dtype, chunk, extra):
+    cols = 128 * chunk + extra
+    x = case(3, cols, dtype, seed=30 + extra)
+    say(f"[gpu] fa_softmax {dtype} 3 x {cols} (one-pass chunk limit {'+1' if extra else ''})")
+    y, lse = run(x)
+    check_rows(to_host(x), y, lse, f"{dtype} 3x{cols}", dtype)
+    _, lse_only = run(x, lse_only=True)
+    check_rows(to_host(x), None, lse_only, f"lse-only {dtype} 3x{cols}", dtype)
+
+
+def test_widest_accepted_row():
+    # the widest row the library takes (2^30 elements: its chunk indices stay
+    # 32-bit), checked on the log-sum-exp; one element more is rejected
+    cols = 1 << 30
+    x = case(1, cols, torch.bfloat16, seed=40)
+    say(f"[gpu] fa_softmax bf16 1 x {cols} (widest accepted), lse only")
+    _, lse = run(x, lse_only=True)
+    check_rows(to_host(x), None, lse, f"bf16 1x{cols}", torch.bfloat16)
+    del x
+    torch.cuda.empty_cache()
+    x1 = torch.empty((1, cols + 1), dtype=torch.bfloat16, device=DEV)
+    l1 = torch.empty((1,), dtype=torch.float32, device=DEV)
+    with pytest.raises(fa.FaError, match="FA_ERR_INVALID_ARG"):
+        fa.fa_softmax(x1, None, l1)
