@@ -52,7 +52,7 @@
 //     d = 128 without spills.  K runs two tiles ahead, V one: iteration t
 //     loads K(t+2) into the stage K(t) left and V(t+1) into the stage V(t-1)
 //     left, and they land before the iteration's only barrier.
-//   * Small non-causal grids (at most one query block per CU): each block's
+//   * Small grids (at most one query block per CU): each block's
 //     key tiles are split in two halves run by two groups of four waves in
 //     one workgroup, each with its own LDS stages and its own (m, l, o); at
 //     the end group 1 hands its state to group 0 through LDS and group 0
@@ -88,9 +88,9 @@ constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs
 
 template <int N_> struct IntC { static constexpr int value = N_; };
 
-// d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.  KSPLIT = 2
-// (non-causal only): two groups of four waves share each query block, group g
-// taking the g-th half of its key tiles; their states are merged at the end.
+// d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.  KSPLIT = 2:
+// two groups of four waves share each query block, group g taking the g-th
+// half of its key tiles; their states are merged at the end.
 template <int D, bool CAUSAL, int KSPLIT>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 :
     // choice neutral)
     constexpr int kPrioPhase = D == 64 ? 2 : 1;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
-    static_assert(KSPLIT == 1 || (KSPLIT == 2 && !CAUSAL), "key split: non-causal only");
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "one or two key groups");
 
     // one array per stage, so that the stage a load fills and the stage the
     // MFMAs read are distinct objects (with a key split: one half per group)
@@ -176,11 +176,13 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 :
     const int tbase = grp * half;
     const int ntg = KSPLIT == 1 ? ntiles : (grp ? ntiles - half : half);
     const int nloop = half;
-    // tiles this wave sees: a prefix of its group's tiles
+    // tiles this wave sees: a prefix of the block's tiles (all of them unless
+    // causal), of which its group takes the part from tbase on
     int nt_w = 0;
     if (wq_first <= wq_last) {
         const int last_key = wq_last + off;
-        nt_w = !CAUSAL ? ntg : (last_key < 0 ? 0 : min(ntiles, last_key / kBc + 1));
+        const int seen = !CAUSAL ? ntiles : (last_key < 0 ? 0 : min(ntiles, last_key / kBc + 1));
+        nt_w = min(max(seen - tbase, 0), ntg);
     }
 
     u32x4_t qf[KK];
@@ -483,15 +485,13 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     const long long BH = (long long)a.B * a.H;
     const long long nblocks = BH * n_qtiles;
     const int xcd_interleave = (BH % 8 == 0) ? 1 : 0;
-    // a non-causal grid of at most one block per CU leaves each CU with one
-    // four-wave workgroup (one wave per SIMD): split every block's keys over
-    // two groups of four waves instead.  Such a workgroup needs the LDS of two
-    // and runs one per CU, so with more blocks than CUs it would take more
-    // dispatch rounds than the unsplit grid (measured slower at 512 blocks).
-    if constexpr (!CAUSAL) {
-        if (nblocks <= cu_count())
-            return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, xcd_interleave, stream);
-    }
+    // a grid of at most one block per CU leaves each CU with one four-wave
+    // workgroup (one wave per SIMD): split every block's keys over two groups
+    // of four waves instead.  Such a workgroup needs the LDS of two and runs
+    // one per CU, so with more blocks than CUs it would take more dispatch
+    // rounds than the unsplit grid (measured slower at 512 blocks).
+    if (nblocks <= cu_count())
+        return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, xcd_interleave, stream);
     return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, xcd_interleave, stream);
 }
 

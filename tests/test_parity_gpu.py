@@ -84,11 +84,12 @@ def test_bf16_key_lens(d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("extra_heads", [0, 1])
-def test_bf16_key_split_grid_boundary(d, extra_heads):
-    # a non-causal grid of at most one query block per CU runs each block's keys in
-    # two halves merged at the end; one more head per batch puts the same inputs on the
-    # unsplit path.  Key lengths: none (the block leaves at once), one tile split 1 / 0,
-    # tile edges, odd tile counts, full.
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_key_split_grid_boundary(d, extra_heads, causal):
+    # a grid of at most one query block per CU runs each block's keys in two halves
+    # merged at the end; one more head per batch puts the same inputs on the unsplit
+    # path.  Key lengths: none (the block leaves at once), one tile split 1 / 0, tile
+    # edges, odd tile counts, full; causal with Nk > N puts the diagonal in the second half.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, N, Nk = 8, 100, 300
     H = cus // B + extra_heads
@@ -96,7 +97,7 @@ def test_bf16_key_split_grid_boundary(d, extra_heads):
     inp = random_case(B, H, N, Nk, d, BF16, seed=41 + d, device=DEV, key_lens=kl)
     rows = sample_rows(B, H, N, per_head=8, seed=d, bh_limit=40)
     rows += [b * H * N + i for b in range(B) for i in (0, N - 1)]
-    forward_and_check(inp, False, what=f"bf16 {B * H} blocks vs {cus} CUs", rows=sorted(set(rows)))
+    forward_and_check(inp, causal, what=f"bf16 {B * H} blocks vs {cus} CUs", rows=sorted(set(rows)))
 
 
 @pytest.mark.parametrize("d", [64, 128])
