@@ -92,7 +92,7 @@ template <int N_> struct IntC { static constexpr int value = N_; };
 // two groups of four waves share each query block, group g taking the g-th
 // half of its key tiles; their states are merged at the end.
 template <int D, bool CAUSAL, int KSPLIT>
-__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 :
     // choice neutral)
     constexpr int kPrioPhase = D == 64 ? 2 : 1;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
-    static_assert(KSPLIT == 1 || KSPLIT == 2, "one or two key groups");
+    static_assert(KSPLIT >= 1 && KSPLIT <= 3, "one to three key groups");
 
     // one array per stage, so that the stage a load fills and the stage the
     // MFMAs read are distinct objects (with a key split: one half per group)
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 :
     // groups pass nloop barriers in the tile loop
     const int half = (ntiles + KSPLIT - 1) / KSPLIT;
     const int tbase = grp * half;
-    const int ntg = KSPLIT == 1 ? ntiles : (grp ? ntiles - half : half);
+    const int ntg = min(max(ntiles - tbase, 0), half);
     const int nloop = half;
     // tiles this wave sees: a prefix of the block's tiles (all of them unless
     // causal), of which its group takes the part from tbase on
@@ -400,39 +400,43 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 2 ? 1 : (D == 64 ? 3 :
         wait_vmem_all();
         __syncthreads();
     }
-    if constexpr (KSPLIT == 2) {
-        // group 1 hands its (reference, l, o) to group 0 through the V stages
-        // (every wave is past its last LDS read and no load is in flight): one
-        // 256-byte row per register, lane-indexed
+    if constexpr (KSPLIT > 1) {
+        // groups 1.. hand their (reference, l, o) to group 0 through the V
+        // stages (every wave is past its last LDS read and no load is in
+        // flight): one 256-byte row per register, lane-indexed
         constexpr int RW = 16 * CB + 2;                      // rows per wave
         constexpr int R0 = (int)(sizeof(Vs0) / 256);         // rows in Vs0
-        static_assert(kWaves * RW <= 2 * R0, "merge rows do not fit the V stages");
-        auto mrow = [&](int k) -> float * {
-            const int r = wave * RW + k;
+        static_assert((KSPLIT - 1) * kWaves * RW <= 2 * R0, "merge rows do not fit the V stages");
+        auto mrow = [&](int from, int k) -> float * {
+            const int r = ((from - 1) * kWaves + wave) * RW + k;
             return (r < R0 ? (float *)Vs0 + 64 * r : (float *)Vs1 + 64 * (r - R0)) + lane;
         };
-        if (grp == 1) {
+        if (grp > 0) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) *mrow(16 * cb + v) = acc[cb][v];
-            *mrow(16 * CB) = ms;
-            *mrow(16 * CB + 1) = l;
+                for (int v = 0; v < 16; ++v) *mrow(grp, 16 * cb + v) = acc[cb][v];
+            *mrow(grp, 16 * CB) = ms;
+            *mrow(grp, 16 * CB + 1) = l;
         }
         __syncthreads();
-        if (grp == 1) return;
-        // merge ('Online Softmax & FlashAttention', Step 1): common reference
-        // m = max(m0, m1), each side scaled by 2^(m_g - m), 0 for a side without keys
-        const float ms1 = *mrow(16 * CB), l1 = *mrow(16 * CB + 1);
-        const float mm = fmaxf(ms, ms1);
-        const float a0 = ms == neg_inf() ? 0.f : exp2_hw(ms - mm);
-        const float a1 = ms1 == neg_inf() ? 0.f : exp2_hw(ms1 - mm);
-        l = a0 * l + a1 * l1;
+        if (grp > 0) return;
+        // merge in group order ('Online Softmax & FlashAttention', Step 1):
+        // common reference m = max(m0, m1), each side scaled by 2^(m_g - m),
+        // 0 for a side without keys
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int from = 1; from < KSPLIT; ++from) {
+            const float ms1 = *mrow(from, 16 * CB), l1 = *mrow(from, 16 * CB + 1);
+            const float mm = fmaxf(ms, ms1);
+            const float a0 = ms == neg_inf() ? 0.f : exp2_hw(ms - mm);
+            const float a1 = ms1 == neg_inf() ? 0.f : exp2_hw(ms1 - mm);
+            l = a0 * l + a1 * l1;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[cb][v] = a0 * acc[cb][v] + a1 * *mrow(16 * cb + v);
-        ms = mm;
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[cb][v] = a0 * acc[cb][v] + a1 * *mrow(from, 16 * cb + v);
+            ms = mm;
+        }
     }
 
     // epilogue: O = o / l (0 for a row without keys), LSE = ms + log2 l in nats (-inf then)
