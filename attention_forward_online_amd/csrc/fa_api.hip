@@ -1,6 +1,7 @@
 // fa_api.hip -- the C ABI declared in include/fa.h: argument checks, kernel
 // selection and launch-error reporting.  Every check happens on the host
 // before any launch; nothing here allocates device memory.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -31,6 +32,24 @@ constexpr long long kMaxSliceBytes = (1LL << 31) - 256;   // per (b, h) slice
 constexpr long long kMaxSoftmaxCols = 1LL << 30;         // chunk indices stay 32-bit
 
 }  // namespace
+
+namespace fa {
+
+int device_cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace fa
 
 extern "C" {
 

@@ -73,8 +73,11 @@ __device__ __forceinline__ void block_of(int bid, int nblk, int xcd_interleave, 
 }
 
 // dQ: 4 waves x 32 queries, K/V tiles of 64 keys through two LDS stages.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+// KSPLIT = 2 (grids of at most one query block per CU): two groups of four
+// waves share the block, group g taking the g-th half of its key tiles with
+// its own stages; the partial dQ sums are added through LDS at the end.
+template <int D, bool CAUSAL, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, uint16_t *__restrict__ dQ, float *__restrict__ L2,
@@ -86,20 +89,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
     // one array per stage: the stage being loaded and the stage being read
     // are distinct objects, so no LDS read waits for the loads in flight
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE], Ks1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE], Vs1[TILE];
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "one or two key groups");
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KSPLIT * TILE], Ks1[KSPLIT * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KSPLIT * TILE], Vs1[KSPLIT * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave >= 0 && wave < kWaves);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave_id >= 0 && wave_id < kWaves * KSPLIT);
+    const int grp = wave_id >> 2;               // key-split group
+    const int wave = wave_id & (kWaves - 1);    // wave within the group: its 32 query rows
     const int li = lane & 31, g = lane >> 5;
     const int krow = perm32(li);
     // K^T operand through the transpose read (the forward's V^T read): lane li
     // receives K column perm32(li) of 4 consecutive keys per read
     const int trow = (li & 15) >> 2;
     const int tcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    auto kst = [&](int stage) -> uint16_t * { return stage ? Ks1 : Ks0; };
-    auto vst = [&](int stage) -> uint16_t * { return stage ? Vs1 : Vs0; };
+    auto kst = [&](int stage) -> uint16_t * { return (stage ? Ks1 : Ks0) + grp * TILE; };
+    auto vst = [&](int stage) -> uint16_t * { return (stage ? Vs1 : Vs0) + grp * TILE; };
 
     int bh, rank;
     block_of(blockIdx.x, n_qtiles, xcd_interleave, bh, rank);
@@ -114,6 +120,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     int kv_end = kv_lim;
     if (CAUSAL) kv_end = min(kv_end, min(q0 + kBq, N) - 1 + off + 1);
     const int ntiles = kv_end > 0 ? (kv_end + kTile - 1) / kTile : 0;
+    // the group's key tiles: tbase .. tbase + half - 1 (those past ntiles only
+    // join the barriers)
+    const int half = (ntiles + KSPLIT - 1) / KSPLIT;
+    const int tbase = grp * half;
     const int wq_first = q0 + wave * 32;
     const int wq_last = min(wq_first + 32, N) - 1;
     const int qrow = wq_first + li;
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     // LSE2 and -D of the rows, for the dK/dV kernel that runs next (it starts
     // its dP accumulators at -D), in per-head arrays of Npad = N rounded up to
     // the 64-query tile; the padding gets zeros (its queries are masked there)
-    if (g == 0 && qrow < Npad) {
+    if (grp == 0 && g == 0 && qrow < Npad) {
         L2[(size_t)bh * Npad + qrow] = qrow < N ? l2 : 0.f;
         Dd[(size_t)bh * Npad + qrow] = qrow < N ? -dd : 0.f;
     }
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     auto tile = [&](auto par_c, int t) {
         constexpr int cur = decltype(par_c)::value;
         refill(t + 1, cur ^ 1);   // lands before this iteration's barrier
-        if (active(t)) {
+        if (t < ntiles && active(t)) {
             f32x16_t s[2], dp[2];
             uint32_t pk[2][8];
             const int j0 = t * kTile;
@@ -285,15 +295,40 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         wait_vmem_all();
         __syncthreads();
     };
-    refill(0, 0);
+    refill(tbase, 0);
     wait_vmem_all();
     __syncthreads();
-    int t = 0;
-    for (; t + 2 <= ntiles; t += 2) {
-        tile(IntC<0>{}, t);
-        tile(IntC<1>{}, t + 1);
+    int u = 0;   // the group's tile index
+    for (; u + 2 <= half; u += 2) {
+        tile(IntC<0>{}, tbase + u);
+        tile(IntC<1>{}, tbase + u + 1);
     }
-    if (t < ntiles) tile(IntC<0>{}, t);
+    if (u < half) tile(IntC<0>{}, tbase + u);
+
+    if constexpr (KSPLIT > 1) {
+        // group 1 hands its partial dQ to group 0 through the V stages (every
+        // wave is past its last LDS read, no load in flight): one 256-byte row
+        // per accumulator register, lane-indexed; group 0 adds it
+        constexpr int RW = 16 * CB;
+        constexpr int R0 = (int)(sizeof(Vs0) / 256);
+        static_assert(kWaves * RW <= 2 * R0, "partial dQ does not fit the V stages");
+        auto mrow = [&](int k) -> float * {
+            const int r = wave * RW + k;
+            return (r < R0 ? (float *)Vs0 + 64 * r : (float *)Vs1 + 64 * (r - R0)) + lane;
+        };
+        if (grp == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) *mrow(16 * cb + v) = acc[cb][v];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[cb][v] += *mrow(16 * cb + v);
+    }
 
     if (qrow < N) {
         uint16_t *grow = dQ + q_base + (size_t)qrow * D;
@@ -590,10 +625,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     if (a.N > 0) {
         // the dQ kernel also writes the D and LSE2 arrays the dK/dV kernel reads
         const int n_qt = (a.N + kBq - 1) / kBq;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(BH * n_qt)), dim3(kThreads), 0,
-                           stream, (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
-                           (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, (uint16_t *)a.dQ, L2,
-                           Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, xcd, c, a.scale);
+        auto dq = [&](auto kern, int threads) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_qt)), dim3(threads), 0, stream,
+                               (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
+                               (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, (uint16_t *)a.dQ,
+                               L2, Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, xcd, c, a.scale);
+        };
+        // at most one query block per CU: two key groups per block
+        if (BH * n_qt <= device_cu_count()) dq(bwd_dq_kernel<D, CAUSAL, 2>, 2 * kThreads);
+        else dq(bwd_dq_kernel<D, CAUSAL, 1>, kThreads);
     }
     if (a.Nk > 0) {
         const int n_kt = (a.Nk + kBk - 1) / kBk;

@@ -63,8 +63,6 @@
 //     the longest blocks; all blocks of a head run on one XCD (the dispatcher
 //     deals workgroup ids to the 8 XCDs round-robin), so K/V re-reads of a
 //     head hit one L2, and consecutive heads go to different XCDs.
-#include <atomic>
-
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -458,20 +456,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     }
 }
 
-// CUs of the current device, looked up once per device
-int cu_count() {
-    constexpr int kMaxDev = 64;
-    static std::atomic<int> cache[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (!v) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cache[dev].store(v, std::memory_order_relaxed);
-    }
-    return v;
-}
 
 template <int D, bool CAUSAL, int KSPLIT>
 hipError_t launch_one(const FwdArgs &a, int n_qtiles, long long nblocks, int xcd_interleave,
@@ -494,7 +478,7 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     // of four waves instead.  Such a workgroup needs the LDS of two and runs
     // one per CU, so with more blocks than CUs it would take more dispatch
     // rounds than the unsplit grid (measured slower at 512 blocks).
-    if (nblocks <= cu_count())
+    if (nblocks <= device_cu_count())
         return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, xcd_interleave, stream);
     return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, xcd_interleave, stream);
 }
