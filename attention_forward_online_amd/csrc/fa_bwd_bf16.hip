@@ -348,10 +348,12 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_
 // dK, dV: 4 waves x 32 keys; Q/dO tiles of 64 queries through two LDS stages.
 // MODE 0 computes both; at d = 128 both accumulators do not fit next to the
 // operands, so MODE 1 (dV only: S, P, dV) and MODE 2 (dK only: S, dP, dS, dK)
-// run as two launches.
+// run as two launches.  KSPLIT = 2 (grids of at most one key block per CU):
+// two groups of four waves share the block, group g taking the g-th half of
+// its query tiles with its own stages; the partial sums are added through LDS.
 enum { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
-template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL, int MODE, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, const float *__restrict__ L2, const float *__restrict__ Dd,
@@ -364,20 +366,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 
     // one array per stage (see the dQ kernel); LD holds the tile's 64 LSE2
     // values followed by its 64 D values
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE], Qs1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Gs0[TILE], Gs1[TILE];   // dO
-    __shared__ __attribute__((aligned(16))) float LD0[2 * kTile], LD1[2 * kTile];
+    static_assert(KSPLIT == 1 || KSPLIT == 2, "one or two query groups");
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[KSPLIT * TILE], Qs1[KSPLIT * TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Gs0[KSPLIT * TILE], Gs1[KSPLIT * TILE];   // dO
+    __shared__ __attribute__((aligned(16))) float LD0[KSPLIT * 2 * kTile], LD1[KSPLIT * 2 * kTile];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave >= 0 && wave < kWaves);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave_id >= 0 && wave_id < kWaves * KSPLIT);
+    const int grp = wave_id >> 2;               // query-split group
+    const int wave = wave_id & (kWaves - 1);    // wave within the group: its 32 keys
     const int li = lane & 31, g = lane >> 5;
     const int qperm = perm32(li);
     const int trow = (li & 15) >> 2;
     const int tcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
-    auto qst = [&](int stage) -> uint16_t * { return stage ? Qs1 : Qs0; };
-    auto gst = [&](int stage) -> uint16_t * { return stage ? Gs1 : Gs0; };
-    auto ldst = [&](int stage) -> float * { return stage ? LD1 : LD0; };
+    auto qst = [&](int stage) -> uint16_t * { return (stage ? Qs1 : Qs0) + grp * TILE; };
+    auto gst = [&](int stage) -> uint16_t * { return (stage ? Gs1 : Gs0) + grp * TILE; };
+    auto ldst = [&](int stage) -> float * { return (stage ? LD1 : LD0) + grp * 2 * kTile; };
 
     int bh, rank;
     block_of(blockIdx.x, n_ktiles, xcd_interleave, bh, rank);
@@ -398,6 +403,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const int t_first = k0 < kv_lim ? i_first / kTile : 0;
     const int n_q = (N + kTile - 1) / kTile;
     const int ntiles = (k0 < kv_lim && i_first < N) ? n_q - t_first : 0;
+    // the group's query tiles: tbase .. tbase + half - 1 (those past ntiles
+    // only join the barriers)
+    const int half = (ntiles + KSPLIT - 1) / KSPLIT;
+    const int tbase = grp * half;
 
     const rsrc_t ksrc = make_rsrc(K + kv_base, (uint32_t)Nk * D * 2);
     const rsrc_t vsrc = make_rsrc(V + kv_base, (uint32_t)Nk * D * 2);
@@ -482,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     auto tile = [&](auto par_c, int t) {
         constexpr int cur = decltype(par_c)::value;
         refill(t + 1, cur ^ 1);   // lands before this iteration's barrier
-        if (active(t)) {
+        if (t < ntiles && active(t)) {
             const int i0 = (t_first + t) * kTile;
             const uint16_t *Qc = qst(cur), *Gc = gst(cur);
             const float *LDc = ldst(cur);
@@ -584,15 +593,50 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
         wait_vmem_all();
         __syncthreads();
     };
-    refill(0, 0);
+    refill(tbase, 0);
     wait_vmem_all();
     __syncthreads();
-    int t = 0;
-    for (; t + 2 <= ntiles; t += 2) {
-        tile(IntC<0>{}, t);
-        tile(IntC<1>{}, t + 1);
+    int u = 0;   // the group's tile index
+    for (; u + 2 <= half; u += 2) {
+        tile(IntC<0>{}, tbase + u);
+        tile(IntC<1>{}, tbase + u + 1);
     }
-    if (t < ntiles) tile(IntC<0>{}, t);
+    if (u < half) tile(IntC<0>{}, tbase + u);
+
+    if constexpr (KSPLIT > 1) {
+        // group 1 hands its partial sums to group 0 through the Q and dO stages
+        // (every wave is past its last LDS read, no load in flight): one
+        // 256-byte row per accumulator register, lane-indexed
+        constexpr int NA = (WANT_DK ? 1 : 0) + (WANT_DV ? 1 : 0);
+        constexpr int RW = 16 * CB * NA;
+        constexpr int R0 = (int)(sizeof(Qs0) / 256);
+        static_assert(kWaves * RW <= 4 * R0, "partial sums do not fit the stages");
+        auto mrow = [&](int k) -> float * {
+            const int r = wave * RW + k, a = r / R0, rr = r - a * R0;
+            uint16_t *base = a == 0 ? Qs0 : a == 1 ? Qs1 : a == 2 ? Gs0 : Gs1;
+            return (float *)base + 64 * rr + lane;
+        };
+        // dK partials in rows 0 .. 16 CB - 1 of the wave's range, dV after them
+        constexpr int VOFF = WANT_DK ? 16 * CB : 0;
+        if (grp == 1) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    if constexpr (WANT_DK) *mrow(16 * cb + v) = adk[cb][v];
+                    if constexpr (WANT_DV) *mrow(VOFF + 16 * cb + v) = adv[cb][v];
+                }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if constexpr (WANT_DK) adk[cb][v] += *mrow(16 * cb + v);
+                if constexpr (WANT_DV) adv[cb][v] += *mrow(VOFF + 16 * cb + v);
+            }
+    }
 
     // accumulator register 8h + e of block cb holds d = 32cb + 16h + 8g + e of this lane's key
     if (key < Nk) {
@@ -637,17 +681,23 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     }
     if (a.Nk > 0) {
         const int n_kt = (a.Nk + kBk - 1) / kBk;
-        auto dkdv = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kt)), dim3(kThreads), 0, stream,
+        auto dkdv = [&](auto kern, int threads) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kt)), dim3(threads), 0, stream,
                                (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                                (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
                                a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, xcd, c, a.scale);
         };
+        // at most one key block per CU: two query groups per block
+        const bool split = BH * n_kt <= device_cu_count();
         if constexpr (D == 64) {
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth>);
+            if (split) dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth, 2>, 2 * kThreads);
+            else dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth, 1>, kThreads);
+        } else if (split) {
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV, 2>, 2 * kThreads);
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK, 2>, 2 * kThreads);
         } else {
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV>);
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK>);
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV, 1>, kThreads);
+            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK, 1>, kThreads);
         }
     }
     return hipGetLastError();

@@ -140,6 +140,25 @@ def test_deterministic():
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("extra_heads", [0, 1])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_grid_boundary(d, causal, extra_heads):
+    # a grid of at most one block per CU runs each block's tiles in two halves whose
+    # partial sums are added at the end: the key tiles of a 128-query dQ block, the
+    # query tiles of a 128-key dK/dV block (N = 300 and Nk = 330 give three blocks per
+    # head in both kernels); one more head per batch puts the same inputs on the
+    # unsplit path.  Key lengths: one tile (split 1 / 0), two tiles, an odd count, all;
+    # causal with Nk > N puts the diagonal in the second half.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, N, Nk = 4, 300, 330
+    H = cus // (B * 3) + extra_heads
+    q, k, v, do, kl = make(B, H, N, Nk, seed=61 + d, key_lens=[1, 65, 200, 330], d=d)
+    heads = sorted({0, 1, H - 1, H + 2, 2 * H + 5, 3 * H + H // 2, B * H - 1})
+    run_and_check(q, k, v, do, kl, causal, heads=heads,
+                  what=f"{B * H * 3} blocks vs {cus} CUs")
+
+
 def test_full_size_headline_shape():
     # B4 H16 N=Nk=2048 d64 causal, the forward's headline shape; two heads in full
     w = synth.WORKLOADS["causal_bf16_b4h16_n2048_d64"]
