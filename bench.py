@@ -114,6 +114,8 @@ def main():
                     help="time only the backward on the headline shape (used under the profiler)")
     ap.add_argument("--only-softmax", action="store_true",
                     help="time only the row softmax (used under the profiler)")
+    ap.add_argument("--only-long", action="store_true",
+                    help="time only the 8192-long d=128 causal prefill (used under the profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE "
                          "counters scale the kernel's counters to bytes")
@@ -153,7 +155,7 @@ def main():
     lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
     # one fa_forward call launches exactly one kernel, so the time per step is
     # that kernel's average launch duration (plus any gap between launches)
-    side_only = args.only_decode or args.only_softmax or args.only_backward
+    side_only = args.only_decode or args.only_softmax or args.only_backward or args.only_long
     ms_step = time_region(lambda: fa.fa_forward(q, k, v, o, lse, causal=True),
                           args.steps if not side_only else 1,
                           args.warmup if not side_only else 0)
@@ -187,7 +189,7 @@ def main():
 
     if side_only:
         out = {"metric": METRIC}
-    if not args.only_headline and not args.only_softmax and not args.only_backward:
+    if not (args.only_headline or args.only_softmax or args.only_backward or args.only_long):
         # ------------------------------------------------------------ decode
         wd = WORKLOADS[DECODE]
         di = make_inputs(wd, device=dev)
@@ -214,7 +216,7 @@ def main():
         del di, od, ld, ws
         torch.cuda.empty_cache()
 
-    if not args.only_headline and not args.only_decode and not args.only_softmax:
+    if not (args.only_headline or args.only_decode or args.only_softmax or args.only_long):
         # ------------------------------------------------ backward (headline shape)
         from attention_forward_online_amd.synth import randn_slices
         dob = randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", dev)
@@ -253,7 +255,7 @@ def main():
         }
         del o1, l1, wv1
 
-    if not args.only_headline and not args.only_decode and not args.only_backward:
+    if not (args.only_headline or args.only_decode or args.only_backward or args.only_long):
         # ------------------------------------------------------- row softmax
         wsm = SOFTMAX_WORKLOADS[SOFTMAX]
         xs = make_softmax_input(wsm, device=dev)
@@ -279,14 +281,14 @@ def main():
     if not (args.only_headline or args.only_decode or args.only_softmax or args.only_backward):
         # ------------------------------------------------- other prefill shapes
         others = {}
-        for name in ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",
-                     "tiny_f32_b1h1_n256_d64"):
+        names = ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128", "tiny_f32_b1h1_n256_d64")
+        for name in names[:1] if args.only_long else names:
             wo = WORKLOADS[name]
             oi = make_inputs(wo, device=dev)
             oo = torch.empty_like(oi["q"])
             ol = torch.empty(wo.B, wo.H, wo.N, device=dev, dtype=torch.float32)
             kl = oi["key_lens"]
-            st = max(5, args.steps // 5)
+            st = args.steps if args.only_long else max(5, args.steps // 5)
             ms_o = time_region(
                 lambda: fa.fa_forward(oi["q"], oi["k"], oi["v"], oo, ol, causal=wo.causal,
                                       key_lens=kl), st, 3)
@@ -302,7 +304,7 @@ def main():
             else:
                 rec["frac"] = round(nominal / (ms_o * 1e-3) / 1e12 / peak, 4)
             rec["peak"] = peak
-            if name == "causal_bf16_b1h32_n8192_d128":
+            if name == "causal_bf16_b1h32_n8192_d128" and not args.only_long:
                 # backward of the same shape (5-GEMM convention, 2.5 x forward FLOPs)
                 from attention_forward_online_amd.synth import randn_slices
                 dg = randn_slices(tuple(oi["q"].shape), 1.0, torch.bfloat16, 0, wo.name, "do", dev)
