@@ -83,6 +83,8 @@ constexpr int kPadK = 8;
 constexpr int kPadV = 32;
 constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
 constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
+// launch orders of the query blocks (workgroup id -> head, block)
+constexpr int kOrderPlain = 0, kOrderXcd = 1, kOrderByKeyLen = 2;
 
 template <int N_> struct IntC { static constexpr int value = N_; };
 
@@ -93,7 +95,7 @@ template <int D, bool CAUSAL, int KSPLIT>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
-    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int xcd_interleave,
+    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int n_qtiles, int order,
     float c) {
     constexpr int KS = D + kPadK;               // K row stride in LDS (elements)
     constexpr int VS = D + kPadV;               // V row stride in LDS (elements)
@@ -134,7 +136,26 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     const int BH = gridDim.x / n_qtiles;
     const int bid = blockIdx.x;
     int rank, bh;                   // rank: position of the block in launch order
-    if (xcd_interleave) {
+    if (order == kOrderByKeyLen) {
+        // batches in descending order of visible keys (ties by batch index), all
+        // blocks of one batch before the next: the blocks with the most work go
+        // out first and a batch without keys goes last, instead of taking every
+        // other dispatch slot.  Lane i ranks batch i; the block's batch is the
+        // one whose rank is its position.  Head-fastest within a batch keeps head
+        // h on XCD h % 8 when H is a multiple of 8.
+        const int nb = BH / H, per_b = H * n_qtiles;
+        const int pos = bid / per_b, rem = bid - pos * per_b;
+        const int len = lane < nb ? visible_len(key_lens, lane, Nk) : -1;
+        int my_rank = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int other = __builtin_amdgcn_readlane(len, i);
+            my_rank += (other > len || (other == len && i < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < nb && my_rank == pos);
+        const int batch = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+        rank = rem / H;
+        bh = batch * H + (rem - rank * H);
+    } else if (order == kOrderXcd) {
         const int hpx = BH >> 3, slot = bid >> 3;
         rank = slot / hpx;
         bh = (slot % hpx) * 8 + (bid & 7);
@@ -458,12 +479,12 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
 
 
 template <int D, bool CAUSAL, int KSPLIT>
-hipError_t launch_one(const FwdArgs &a, int n_qtiles, long long nblocks, int xcd_interleave,
+hipError_t launch_one(const FwdArgs &a, int n_qtiles, long long nblocks, int order,
                       hipStream_t stream) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, KSPLIT>), dim3((unsigned)nblocks),
                        dim3(kThreads * KSPLIT), 0, stream, (const uint16_t *)a.Q,
                        (const uint16_t *)a.K, (const uint16_t *)a.V, (uint16_t *)a.O, a.LSE,
-                       a.key_lens, a.H, a.N, a.Nk, n_qtiles, xcd_interleave, a.scale * kLog2e);
+                       a.key_lens, a.H, a.N, a.Nk, n_qtiles, order, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -472,15 +493,20 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
     const long long BH = (long long)a.B * a.H;
     const long long nblocks = BH * n_qtiles;
-    const int xcd_interleave = (BH % 8 == 0) ? 1 : 0;
+    // launch order: non-causal grids with per-batch key lengths (up to 64
+    // batches, one lane each) by key length; otherwise head-per-XCD when B*H is
+    // a multiple of 8.  Causal grids keep their longest-first order.
+    const int order = (a.key_lens && !CAUSAL && a.B <= 64) ? kOrderByKeyLen
+                      : (BH % 8 == 0)                       ? kOrderXcd
+                                                            : kOrderPlain;
     // a grid of at most one block per CU leaves each CU with one four-wave
     // workgroup (one wave per SIMD): split every block's keys over two groups
     // of four waves instead.  Such a workgroup needs the LDS of two and runs
     // one per CU, so with more blocks than CUs it would take more dispatch
     // rounds than the unsplit grid (measured slower at 512 blocks).
     if (nblocks <= device_cu_count())
-        return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, xcd_interleave, stream);
-    return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, xcd_interleave, stream);
+        return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, order, stream);
+    return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, order, stream);
 }
 
 }  // namespace

@@ -82,6 +82,28 @@ def test_bf16_key_lens(d, causal):
     forward_and_check(inp, causal, what="bf16 key_lens")
 
 
+@pytest.mark.parametrize("B,H,N,Nk,d", [(64, 2, 70, 150, 64), (64, 8, 300, 200, 128),
+                                          (3, 5, 257, 300, 64), (65, 1, 64, 64, 64)])
+def test_bf16_key_length_launch_order(B, H, N, Nk, d):
+    # non-causal grids with key lengths and at most 64 batches go out batch by batch in
+    # descending order of visible keys, each workgroup finding its batch from the ranks
+    # of all batches: every (head, block) must be computed exactly once.  Key lengths
+    # with ties, 0, Nk, past Nk and negative; 128 blocks (key split), 1536 blocks, heads
+    # not a multiple of 8, and 65 batches (the head-per-XCD order instead).  Outputs
+    # start as NaN, so a block left out or written twice with the wrong rows shows.
+    rng = np.random.default_rng(B * 1000 + N)
+    kl = [int(x) for x in rng.choice([0, 1, 37, Nk // 2, Nk // 2, Nk, Nk + 9, -3], size=B)]
+    inp = random_case(B, H, N, Nk, d, BF16, seed=B + d, device=DEV, key_lens=kl)
+    o = torch.full_like(inp["q"], float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=DEV)
+    say(f"[gpu] fa_forward key-length order B={B} H={H} N={N} Nk={Nk} d={d} key_lens={kl}")
+    fa.fa_forward(inp["q"], inp["k"], inp["v"], o, lse, causal=False, key_lens=inp["key_lens"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(to_host(inp["q"]), to_host(inp["k"]), to_host(inp["v"]),
+                                    scale=float(np.float32(1.0 / np.sqrt(d))), key_lens=kl)
+    compare(o, lse, O_ref, L_ref, BF16, f"key-length order B={B}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("extra_heads", [0, 1])
 @pytest.mark.parametrize("causal", [False, True])
