@@ -58,20 +58,6 @@ template <int D> constexpr int kRowElems = D == 64 ? D + 8 : D + 24;
 template <int D>
 __device__ __forceinline__ int lds_at(int row, int col) { return row * kRowElems<D> + col; }
 
-// Workgroup -> (head, block rank); with B*H divisible by 8 all blocks of a
-// head run on one XCD (round-robin dispatch), as in the forward.
-__device__ __forceinline__ void block_of(int bid, int nblk, int xcd_interleave, int &bh, int &rank) {
-    const int BH = gridDim.x / nblk;
-    if (xcd_interleave) {
-        const int hpx = BH >> 3, slot = bid >> 3;
-        rank = slot / hpx;
-        bh = (slot % hpx) * 8 + (bid & 7);
-    } else {
-        rank = bid / BH;
-        bh = bid % BH;
-    }
-}
-
 // dQ: 4 waves x 32 queries, K/V tiles of 64 keys through two LDS stages.
 // KSPLIT = 2 (grids of at most one query block per CU): two groups of four
 // waves share the block, group g taking the g-th half of its key tiles with
@@ -82,7 +68,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ O, const uint16_t *__restrict__ dO,
     const float *__restrict__ LSE, uint16_t *__restrict__ dQ, float *__restrict__ L2,
     float *__restrict__ Dd, const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad,
-    int n_qtiles, int xcd_interleave, float c, float scale) {
+    int n_qtiles, int order, float c, float scale) {
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
@@ -108,7 +94,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_
     auto vst = [&](int stage) -> uint16_t * { return (stage ? Vs1 : Vs0) + grp * TILE; };
 
     int bh, rank;
-    block_of(blockIdx.x, n_qtiles, xcd_interleave, bh, rank);
+    block_in_order(blockIdx.x, gridDim.x / n_qtiles, n_qtiles, order, H, key_lens, Nk, bh, rank);
     const int b = bh / H;
     const int off = Nk - N;
     const int kv_lim = visible_len(key_lens, b, Nk);
@@ -358,7 +344,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
     uint16_t *__restrict__ dV, const float *__restrict__ L2, const float *__restrict__ Dd,
     const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_ktiles,
-    int xcd_interleave, float c, float scale) {
+    int order, float c, float scale) {
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
@@ -385,7 +371,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
     auto ldst = [&](int stage) -> float * { return (stage ? LD1 : LD0) + grp * 2 * kTile; };
 
     int bh, rank;
-    block_of(blockIdx.x, n_ktiles, xcd_interleave, bh, rank);
+    block_in_order(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, order, H, key_lens, Nk, bh, rank);
     const int b = bh / H;
     const int off = Nk - N;
     const int kv_lim = visible_len(key_lens, b, Nk);
@@ -664,7 +650,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int Npad = (a.N + kTile - 1) / kTile * kTile;
     float *L2 = static_cast<float *>(a.workspace);
     float *Dd = L2 + BH * Npad;
-    const int xcd = (BH % 8 == 0) ? 1 : 0;
+    const int order = launch_order(a.B, a.H, CAUSAL, a.key_lens);
     const float c = a.scale * kLog2e;
     if (a.N > 0) {
         // the dQ kernel also writes the D and LSE2 arrays the dK/dV kernel reads
@@ -673,7 +659,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_qt)), dim3(threads), 0, stream,
                                (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                                (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, (uint16_t *)a.dQ,
-                               L2, Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, xcd, c, a.scale);
+                               L2, Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, order, c, a.scale);
         };
         // at most one query block per CU: two key groups per block
         if (BH * n_qt <= device_cu_count()) dq(bwd_dq_kernel<D, CAUSAL, 2>, 2 * kThreads);
@@ -685,7 +671,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kt)), dim3(threads), 0, stream,
                                (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                                (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
-                               a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, xcd, c, a.scale);
+                               a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, order, c, a.scale);
         };
         // at most one key block per CU: two query groups per block
         const bool split = BH * n_kt <= device_cu_count();

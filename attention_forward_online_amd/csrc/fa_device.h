@@ -158,11 +158,63 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Even split of a clamped key length: the visible keys of batch b.
+// The visible keys of batch b: its key length clamped to [0, Nk] (all Nk
+// without key lengths).
 __device__ __forceinline__ int visible_len(const int32_t *key_lens, int b, int Nk) {
     if (!key_lens) return Nk;
     int kl = key_lens[b];
     return kl < 0 ? 0 : (kl > Nk ? Nk : kl);
+}
+
+// Launch orders of a grid of BH heads x nblk blocks: workgroup id -> (head bh,
+// rank of the block within its head).
+//  kOrderPlain: rank-major, head-fastest.
+//  kOrderXcd (BH a multiple of 8): head bh on XCD bh % 8 (the dispatcher deals
+//    workgroup ids to the XCDs round-robin), so all blocks of a head share one
+//    L2; rank-major within an XCD.
+//  kOrderByKeyLen (per-batch key lengths, at most 64 batches): batch by batch in
+//    descending order of visible keys (ties by batch index), rank-major and
+//    head-fastest within a batch.  Each XCD sends its even- and odd-numbered
+//    workgroups to different halves of its CUs, so an order that alternates a
+//    batch without keys with one with keys leaves half the CUs idle; sorted,
+//    the blocks with work go out first.  Lane i ranks batch i and the block's
+//    batch is the one whose rank is its position: every lane of the wave must
+//    be active.
+constexpr int kOrderPlain = 0, kOrderXcd = 1, kOrderByKeyLen = 2;
+__device__ __forceinline__ void block_in_order(int bid, int BH, int nblk, int order, int H,
+                                               const int32_t *key_lens, int Nk, int &bh,
+                                               int &rank) {
+    if (order == kOrderByKeyLen) {
+        const int lane = threadIdx.x & 63;
+        const int nb = BH / H, per_b = H * nblk;
+        const int pos = bid / per_b, rem = bid - pos * per_b;
+        const int len = lane < nb ? visible_len(key_lens, lane, Nk) : -1;
+        int my_rank = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int other = __builtin_amdgcn_readlane(len, i);
+            my_rank += (other > len || (other == len && i < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < nb && my_rank == pos);
+        const int batch = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+        rank = rem / H;
+        bh = batch * H + (rem - rank * H);
+    } else if (order == kOrderXcd) {
+        const int hpx = BH >> 3, slot = bid >> 3;
+        rank = slot / hpx;
+        bh = (slot % hpx) * 8 + (bid & 7);
+    } else {
+        rank = bid / BH;
+        bh = bid % BH;
+    }
+}
+
+// The launch order for a grid: by key length for non-causal grids with key
+// lengths of at most 64 batches, else head-per-XCD when B*H is a multiple of 8.
+// Causal grids keep their own longest-first order within each head.
+__host__ __device__ inline int launch_order(long long B, long long H, bool causal,
+                                            const int32_t *key_lens) {
+    if (key_lens && !causal && B <= 64) return kOrderByKeyLen;
+    return (B * H) % 8 == 0 ? kOrderXcd : kOrderPlain;
 }
 
 }  // namespace fa

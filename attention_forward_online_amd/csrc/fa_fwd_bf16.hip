@@ -83,8 +83,6 @@ constexpr int kPadK = 8;
 constexpr int kPadV = 32;
 constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
 constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
-// launch orders of the query blocks (workgroup id -> head, block)
-constexpr int kOrderPlain = 0, kOrderXcd = 1, kOrderByKeyLen = 2;
 
 template <int N_> struct IntC { static constexpr int value = N_; };
 
@@ -130,39 +128,11 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     auto kst = [&](int stage) -> uint16_t * { return (stage ? Ks1 : Ks0) + grp * (kBc * KS); };
     auto vst = [&](int stage) -> uint16_t * { return (stage ? Vs1 : Vs0) + grp * (kBc * VS); };
 
-    // workgroup -> (head, query block).  With B*H divisible by 8, head bh lives on
-    // XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs round-robin):
-    // all blocks of a head share one L2 and neighbouring heads spread over XCDs.
+    // workgroup -> (head, query block) in the launch order `order`
     const int BH = gridDim.x / n_qtiles;
     const int bid = blockIdx.x;
     int rank, bh;                   // rank: position of the block in launch order
-    if (order == kOrderByKeyLen) {
-        // batches in descending order of visible keys (ties by batch index), all
-        // blocks of one batch before the next: the blocks with the most work go
-        // out first and a batch without keys goes last, instead of taking every
-        // other dispatch slot.  Lane i ranks batch i; the block's batch is the
-        // one whose rank is its position.  Head-fastest within a batch keeps head
-        // h on XCD h % 8 when H is a multiple of 8.
-        const int nb = BH / H, per_b = H * n_qtiles;
-        const int pos = bid / per_b, rem = bid - pos * per_b;
-        const int len = lane < nb ? visible_len(key_lens, lane, Nk) : -1;
-        int my_rank = 0;
-        for (int i = 0; i < nb; ++i) {
-            const int other = __builtin_amdgcn_readlane(len, i);
-            my_rank += (other > len || (other == len && i < lane)) ? 1 : 0;
-        }
-        const unsigned long long hit = __ballot(lane < nb && my_rank == pos);
-        const int batch = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
-        rank = rem / H;
-        bh = batch * H + (rem - rank * H);
-    } else if (order == kOrderXcd) {
-        const int hpx = BH >> 3, slot = bid >> 3;
-        rank = slot / hpx;
-        bh = (slot % hpx) * 8 + (bid & 7);
-    } else {
-        rank = bid / BH;
-        bh = bid % BH;
-    }
+    block_in_order(bid, BH, n_qtiles, order, H, key_lens, Nk, bh, rank);
     const int b = bh / H;
     const int off = Nk - N;                     // causal: key j visible to query i iff j <= i + off
     const int kv_lim = __builtin_amdgcn_readfirstlane(visible_len(key_lens, b, Nk));
@@ -493,12 +463,7 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
     const long long BH = (long long)a.B * a.H;
     const long long nblocks = BH * n_qtiles;
-    // launch order: non-causal grids with per-batch key lengths (up to 64
-    // batches, one lane each) by key length; otherwise head-per-XCD when B*H is
-    // a multiple of 8.  Causal grids keep their longest-first order.
-    const int order = (a.key_lens && !CAUSAL && a.B <= 64) ? kOrderByKeyLen
-                      : (BH % 8 == 0)                       ? kOrderXcd
-                                                            : kOrderPlain;
+    const int order = launch_order(a.B, a.H, CAUSAL, a.key_lens);
     // a grid of at most one block per CU leaves each CU with one four-wave
     // workgroup (one wave per SIMD): split every block's keys over two groups
     // of four waves instead.  Such a workgroup needs the LDS of two and runs

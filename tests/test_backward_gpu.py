@@ -159,6 +159,17 @@ def test_split_grid_boundary(d, causal, extra_heads):
                   what=f"{B * H * 3} blocks vs {cus} CUs")
 
 
+@pytest.mark.parametrize("B,H,N,Nk,d", [(64, 2, 70, 150, 64), (3, 5, 257, 300, 128)])
+def test_key_length_launch_order(B, H, N, Nk, d):
+    # non-causal grids with key lengths go out batch by batch in descending order of
+    # visible keys in both backward kernels (each workgroup ranks the batches itself):
+    # every (head, block) once, with tied, empty, past-Nk and negative key lengths
+    rng = np.random.default_rng(B * 1000 + N)
+    kl = [int(x) for x in rng.choice([0, 1, 37, Nk // 2, Nk // 2, Nk, Nk + 9, -3], size=B)]
+    q, k, v, do, klt = make(B, H, N, Nk, seed=B + d, key_lens=kl, d=d)
+    run_and_check(q, k, v, do, klt, False, what=f"key-length order B={B}")
+
+
 def test_full_size_headline_shape():
     # B4 H16 N=Nk=2048 d64 causal, the forward's headline shape; two heads in full
     w = synth.WORKLOADS["causal_bf16_b4h16_n2048_d64"]
