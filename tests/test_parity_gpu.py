@@ -104,6 +104,29 @@ def test_bf16_key_length_launch_order(B, H, N, Nk, d):
     compare(o, lse, O_ref, L_ref, BF16, f"key-length order B={B}")
 
 
+@pytest.mark.parametrize("kl", [[0, 300, 300, 0], [500, 300, 200, 100], [500, 300, 200, 0],
+                                [0, 0, 0, 0], [600, 1, 64, 65]])
+def test_bf16_key_length_order_one_to_two_blocks_per_cu(kl):
+    # d = 128, non-causal, key lengths, between one and two blocks per CU (the
+    # masked workload's regime): batches with keys first in the launch order,
+    # batches without keys (O = 0, LSE = -inf) after them, equal and unequal tile
+    # counts side by side.  Outputs start as NaN.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, H, Nk, d = 4, 16, 600, 128
+    n_qt = (3 * cus) // (2 * B * H)
+    N = n_qt * 128 - 28
+    assert cus < B * H * n_qt <= 2 * cus
+    inp = random_case(B, H, N, Nk, d, BF16, seed=sum(kl) + 3, device=DEV, key_lens=kl)
+    o = torch.full_like(inp["q"], float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=DEV)
+    say(f"[gpu] fa_forward key-length order, 1-2 blocks per CU B={B} H={H} N={N} Nk={Nk} key_lens={kl}")
+    fa.fa_forward(inp["q"], inp["k"], inp["v"], o, lse, causal=False, key_lens=inp["key_lens"])
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(to_host(inp["q"]), to_host(inp["k"]), to_host(inp["v"]),
+                                    scale=float(np.float32(1.0 / np.sqrt(d))), key_lens=kl)
+    compare(o, lse, O_ref, L_ref, BF16, f"key-length order, 1-2 blocks per CU {kl}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("extra_heads", [0, 1])
 @pytest.mark.parametrize("causal", [False, True])
