@@ -172,15 +172,19 @@ __device__ __forceinline__ int visible_len(const int32_t *key_lens, int b, int N
 //  kOrderXcd (BH a multiple of 8): head bh on XCD bh % 8 (the dispatcher deals
 //    workgroup ids to the XCDs round-robin), so all blocks of a head share one
 //    L2; rank-major within an XCD.
-//  kOrderByKeyLen (per-batch key lengths, at most 64 batches): batch by batch in
-//    descending order of visible keys (ties by batch index), rank-major and
-//    head-fastest within a batch.  Each XCD sends its even- and odd-numbered
-//    workgroups to different halves of its CUs, so an order that alternates a
-//    batch without keys with one with keys leaves half the CUs idle; sorted,
-//    the blocks with work go out first.  Lane i ranks batch i and the block's
-//    batch is the one whose rank is its position: every lane of the wave must
-//    be active.
+//  kOrderByKeyLen (per-batch key lengths, at most kMaxOrderBatches batches):
+//    batch by batch, rank-major and head-fastest within a batch.  Up to 64
+//    batches go in descending order of visible keys (ties by batch index): lane
+//    i ranks batch i and the block's batch is the one whose rank is its
+//    position.  More batches go with those that have keys first, each part in
+//    index order, from one 64-bit mask of "has keys" per 64 batches (with no
+//    batch empty, the head-per-XCD or plain order instead).  Why: each
+//    XCD sends its even- and odd-numbered workgroups to different halves of its
+//    CUs, so an order that alternates a batch without keys with one with keys
+//    leaves half the CUs idle; this way the blocks with work go out first.
+//    Every lane of the wave must be active.
 constexpr int kOrderPlain = 0, kOrderXcd = 1, kOrderByKeyLen = 2;
+constexpr int kMaxOrderBatches = 1024;     // batches the key-length order handles
 __device__ __forceinline__ void block_in_order(int bid, int BH, int nblk, int order, int H,
                                                const int32_t *key_lens, int Nk, int &bh,
                                                int &rank) {
@@ -188,17 +192,54 @@ __device__ __forceinline__ void block_in_order(int bid, int BH, int nblk, int or
         const int lane = threadIdx.x & 63;
         const int nb = BH / H, per_b = H * nblk;
         const int pos = bid / per_b, rem = bid - pos * per_b;
-        const int len = lane < nb ? visible_len(key_lens, lane, Nk) : -1;
-        int my_rank = 0;
-        for (int i = 0; i < nb; ++i) {
-            const int other = __builtin_amdgcn_readlane(len, i);
-            my_rank += (other > len || (other == len && i < lane)) ? 1 : 0;
-        }
-        const unsigned long long hit = __ballot(lane < nb && my_rank == pos);
-        const int batch = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
         rank = rem / H;
-        bh = batch * H + (rem - rank * H);
-    } else if (order == kOrderXcd) {
+        if (nb <= 64) {
+            const int len = lane < nb ? visible_len(key_lens, lane, Nk) : -1;
+            int my_rank = 0;
+            for (int i = 0; i < nb; ++i) {
+                const int other = __builtin_amdgcn_readlane(len, i);
+                my_rank += (other > len || (other == len && i < lane)) ? 1 : 0;
+            }
+            const unsigned long long hit = __ballot(lane < nb && my_rank == pos);
+            bh = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit)) * H + (rem - rank * H);
+            return;
+        }
+        // more batches: one mask of "has keys" per 64 batches, all loads issued
+        // together; with some batch empty, the pos-th batch of its part
+        unsigned long long has[kMaxOrderBatches / 64];
+        int with = 0;
+#pragma unroll
+        for (int c = 0; c < kMaxOrderBatches / 64; ++c) {
+            const int i = 64 * c + lane;
+            has[c] = __ballot(i < nb && visible_len(key_lens, i, Nk) > 0);
+            with += __builtin_popcountll(has[c]);
+        }
+        if (with < nb) {
+            const bool want = pos < with;
+            int left = want ? pos : pos - with;   // batches of the part still to pass
+            int batch = 0;
+#pragma unroll
+            for (int c = 0; c < kMaxOrderBatches / 64; ++c) {
+                const int cnt = min(64, max(nb - 64 * c, 0));
+                const unsigned long long valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
+                const unsigned long long m = want ? has[c] : (~has[c] & valid);
+                const int n = __builtin_popcountll(m);
+                if (left >= 0 && left < n) {
+                    // the left-th set bit of m: the lane with that many set bits below it
+                    const unsigned long long below = m & ((1ull << lane) - 1ull);
+                    const unsigned long long hit =
+                        __ballot(((m >> lane) & 1ull) && __builtin_popcountll(below) == left);
+                    batch = 64 * c + __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+                }
+                left -= n;
+            }
+            bh = batch * H + (rem - rank * H);
+            return;
+        }
+        // every batch has keys: nothing to move, the order below applies
+        order = BH % 8 == 0 ? kOrderXcd : kOrderPlain;
+    }
+    if (order == kOrderXcd) {
         const int hpx = BH >> 3, slot = bid >> 3;
         rank = slot / hpx;
         bh = (slot % hpx) * 8 + (bid & 7);
@@ -209,11 +250,11 @@ __device__ __forceinline__ void block_in_order(int bid, int BH, int nblk, int or
 }
 
 // The launch order for a grid: by key length for non-causal grids with key
-// lengths of at most 64 batches, else head-per-XCD when B*H is a multiple of 8.
-// Causal grids keep their own longest-first order within each head.
+// lengths, else head-per-XCD when B*H is a multiple of 8.  Causal grids keep
+// their own longest-first order within each head.
 __host__ __device__ inline int launch_order(long long B, long long H, bool causal,
                                             const int32_t *key_lens) {
-    if (key_lens && !causal && B <= 64) return kOrderByKeyLen;
+    if (key_lens && !causal && B <= kMaxOrderBatches) return kOrderByKeyLen;
     return (B * H) % 8 == 0 ? kOrderXcd : kOrderPlain;
 }
 

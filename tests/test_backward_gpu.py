@@ -159,7 +159,8 @@ def test_split_grid_boundary(d, causal, extra_heads):
                   what=f"{B * H * 3} blocks vs {cus} CUs")
 
 
-@pytest.mark.parametrize("B,H,N,Nk,d", [(64, 2, 70, 150, 64), (3, 5, 257, 300, 128)])
+@pytest.mark.parametrize("B,H,N,Nk,d", [(64, 2, 70, 150, 64), (3, 5, 257, 300, 128),
+                                          (200, 2, 70, 150, 64)])
 def test_key_length_launch_order(B, H, N, Nk, d):
     # non-causal grids with key lengths go out batch by batch in descending order of
     # visible keys in both backward kernels (each workgroup ranks the batches itself):

@@ -83,16 +83,21 @@ def test_bf16_key_lens(d, causal):
 
 
 @pytest.mark.parametrize("B,H,N,Nk,d", [(64, 2, 70, 150, 64), (64, 8, 300, 200, 128),
-                                          (3, 5, 257, 300, 64), (65, 1, 64, 64, 64)])
+                                          (3, 5, 257, 300, 64), (65, 1, 64, 64, 64),
+                                          (200, 2, 70, 150, 128), (1024, 1, 16, 40, 64),
+                                          (1025, 1, 16, 40, 64), (96, 8, 64, 100, 64)])
 def test_bf16_key_length_launch_order(B, H, N, Nk, d):
-    # non-causal grids with key lengths and at most 64 batches go out batch by batch in
-    # descending order of visible keys, each workgroup finding its batch from the ranks
-    # of all batches: every (head, block) must be computed exactly once.  Key lengths
-    # with ties, 0, Nk, past Nk and negative; 128 blocks (key split), 1536 blocks, heads
-    # not a multiple of 8, and 65 batches (the head-per-XCD order instead).  Outputs
-    # start as NaN, so a block left out or written twice with the wrong rows shows.
+    # non-causal grids with key lengths go out batch by batch: up to 64 batches in
+    # descending order of visible keys (each workgroup ranks all batches), up to 1024
+    # with the batches that have keys first (per-64 masks), beyond that in the plain
+    # order: every (head, block) must be computed exactly once.  Key lengths with ties,
+    # 0, Nk, past Nk and negative; 128 blocks (key split), 1536 blocks, heads not a
+    # multiple of 8.  Outputs start as NaN, so a block left out or written twice with
+    # the wrong rows shows.  B = 96: more than 64 batches, none empty (the head-per-XCD
+    # order then applies).
     rng = np.random.default_rng(B * 1000 + N)
-    kl = [int(x) for x in rng.choice([0, 1, 37, Nk // 2, Nk // 2, Nk, Nk + 9, -3], size=B)]
+    choices = [1, 37, Nk // 2, Nk, Nk + 9] if B == 96 else [0, 1, 37, Nk // 2, Nk // 2, Nk, Nk + 9, -3]
+    kl = [int(x) for x in rng.choice(choices, size=B)]
     inp = random_case(B, H, N, Nk, d, BF16, seed=B + d, device=DEV, key_lens=kl)
     o = torch.full_like(inp["q"], float("nan"))
     lse = torch.full((B, H, N), float("nan"), device=DEV)
