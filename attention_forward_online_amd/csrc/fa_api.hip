@@ -35,15 +35,23 @@ constexpr long long kMaxSoftmaxCols = 1LL << 30;         // chunk indices stay 3
 
 namespace fa {
 
+// Compute units of the current device, looked up once per device.  A failed
+// query falls back to 256 (MI355X) and clears the runtime's last error, so the
+// launch that follows reports only its own status.
 int device_cu_count() {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cache[kMaxDev];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return 256;
+    }
     int v = cache[dev].load(std::memory_order_relaxed);
     if (!v) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+            (void)hipGetLastError();
             v = 256;
+        }
         cache[dev].store(v, std::memory_order_relaxed);
     }
     return v;

@@ -53,6 +53,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 
 // compute units of the current device (looked up once per device)
 int device_cu_count();
+
 // fp32 prefill, 1 <= d <= 256: fp32 FMA tiles.
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 // split-KV decode, d in {64, 128}; is_bf16 selects the element type.
