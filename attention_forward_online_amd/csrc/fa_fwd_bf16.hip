@@ -85,6 +85,7 @@ constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a resc
 constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
 
 template <int N_> struct IntC { static constexpr int value = N_; };
+template <bool B_> struct BoolC { static constexpr bool value = B_; };
 
 // d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.  KSPLIT = 2:
 // two groups of four waves share each query block, group g taking the g-th
@@ -320,32 +321,46 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     // iteration t: K(t+2) and V(t+1) are loaded into the stages K(t) and
     // V(t-1) left; S(t+1) is computed from K(t+1) beside the exponentials of
     // tile t, then O += P(t) V(t) beside the rest of them and the row max of
-    // tile t+1.  One barrier per iteration.  On a wave's last tile the S(t+1)
-    // products are computed but not used (the stage then holds zeros or
-    // another wave's next tile).
+    // tile t+1.  One barrier per iteration.  A wave's last tile (LAST) has no
+    // S(t+1) to compute, and when keys 32..63 of it are all past the wave's
+    // visible keys (the causal diagonal, a key length) their exponentials and
+    // P.V products are skipped too: those weights are exactly 0, so the result
+    // is the same to the bit.
     auto refill = [&](int par, int t) {   // K(t+2), V(t+1); they land before the barrier
         dma_k(kst(par), t + 2);
         dma_v(vst(par ^ 1), t + 1);
     };
-    auto step = [&](auto par_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    auto step = [&](auto par_c, auto last_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         constexpr int par = decltype(par_c)::value;
+        constexpr bool LAST = decltype(last_c)::value;
         refill(par, t);
         uint32_t pk[4][4];
         float rs[4] = {-0.f, -0.f, -0.f, -0.f};
+        // last tile: keys 32..63 of it all past the wave's visible keys?
+        bool half = false;
+        if constexpr (LAST) {
+            const int j0 = (tbase + t) * kBc;
+            const int vis_last = CAUSAL ? min(kv_lim - 1, wq_last + off) : kv_lim - 1;
+            half = j0 + 32 > vis_last;
+        }
         u32x4_t kop[PD];
+        if constexpr (!LAST) {
 #pragma unroll
-        for (int i = 0; i < PD; ++i) kop[i] = k_operand(par ^ 1, i);
+            for (int i = 0; i < PD; ++i) kop[i] = k_operand(par ^ 1, i);
+        }
         if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
-            if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
-            p_pair(sc, i, pk, rs);
+            if constexpr (!LAST) {
+                sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
+                if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
+            }
+            if (!LAST || !half || i < 8) p_pair(sc, i, pk, rs);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(0);
-        const bool more = t + 1 < nt_w;
-        if (more && need_mask(t + 1)) apply_mask(t + 1, sn);
+        if constexpr (!LAST)
+            if (need_mask(t + 1)) apply_mask(t + 1, sn);
         float m4[4];
         u32x4_t vop[PD];
 #pragma unroll
@@ -354,34 +369,41 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
         for (int i = 0; i < NP2; ++i) {
             const int ci = i / CB;
-            acc[i % CB] = mfma32(vop[i % PD], u32x4_t{pk[ci][0], pk[ci][1], pk[ci][2], pk[ci][3]},
-                                 acc[i % CB]);
+            if (!LAST || !half || ci < 2)
+                acc[i % CB] = mfma32(vop[i % PD], u32x4_t{pk[ci][0], pk[ci][1], pk[ci][2], pk[ci][3]},
+                                     acc[i % CB]);
             if (i + PD < NP2) vop[i % PD] = v_operand(par, i + PD);
-            if (i < PAIRS2 / 2) {
+            if (i < PAIRS2 / 2 && (!LAST || !half)) {
                 p_pair(sc, NS + 2 * i, pk, rs);
                 p_pair(sc, NS + 2 * i + 1, pk, rs);
             }
-            if (i >= NP2 - 4) {
-                m4[i - (NP2 - 4)] = max8(sn, i - (NP2 - 4));
-                pin(m4[i - (NP2 - 4)]);
+            if constexpr (!LAST) {
+                if (i >= NP2 - 4) {
+                    m4[i - (NP2 - 4)] = max8(sn, i - (NP2 - 4));
+                    pin(m4[i - (NP2 - 4)]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (kPrioPhase == 2) __builtin_amdgcn_s_setprio(0);
         l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        if (more) decide(rowmax(m4));
+        if constexpr (!LAST) decide(rowmax(m4));
         wait_vmem_all();
         __syncthreads();
     };
-    // every wave passes ntiles barriers: nt_w in its own tiles, the rest in the
-    // refill-only loop
+    // every wave passes nloop barriers: nt_w in its own tiles (the last one by
+    // the LAST step), the rest in the refill-only loop
     int t = 0;
-    for (; t + 2 <= nt_w; t += 2) {
-        step(IntC<0>{}, t, sa, sb);
-        step(IntC<1>{}, t + 1, sb, sa);
+    for (; t + 2 < nt_w; t += 2) {
+        step(IntC<0>{}, BoolC<false>{}, t, sa, sb);
+        step(IntC<1>{}, BoolC<false>{}, t + 1, sb, sa);
     }
-    if (t < nt_w) {
-        step(IntC<0>{}, t, sa, sb);
+    if (t + 2 == nt_w) {
+        step(IntC<0>{}, BoolC<false>{}, t, sa, sb);
+        step(IntC<1>{}, BoolC<true>{}, t + 1, sb, sa);
+        t += 2;
+    } else if (t + 1 == nt_w) {
+        step(IntC<0>{}, BoolC<true>{}, t, sa, sb);
         ++t;
     }
     for (; t < nloop; ++t) {
