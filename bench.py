@@ -116,10 +116,17 @@ def main():
                     help="time only the row softmax (used under the profiler)")
     ap.add_argument("--only-long", action="store_true",
                     help="time only the 8192-long d=128 causal prefill (used under the profiler)")
+    ap.add_argument("--only-prefill", default=None,
+                    choices=["causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128",
+                             "tiny_f32_b1h1_n256_d64"],
+                    help="time only this prefill workload (used under the profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy, whose FETCH_SIZE / WRITE_SIZE "
                          "counters scale the kernel's counters to bytes")
     args = ap.parse_args()
+    if args.only_long:
+        args.only_prefill = "causal_bf16_b1h32_n8192_d128"
+    args.only_long = args.only_prefill is not None
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(every workload here is measured on a single MI355X)", file=sys.stderr)
@@ -282,7 +289,7 @@ def main():
         # ------------------------------------------------- other prefill shapes
         others = {}
         names = ("causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128", "tiny_f32_b1h1_n256_d64")
-        for name in names[:1] if args.only_long else names:
+        for name in (args.only_prefill,) if args.only_prefill else names:
             wo = WORKLOADS[name]
             oi = make_inputs(wo, device=dev)
             oo = torch.empty_like(oi["q"])
