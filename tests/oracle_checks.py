@@ -89,7 +89,7 @@ def check_x153(lib):
     y, m, l = oracle.softmax(x, lib=lib)
     l_closed = math.exp(-4.0) + 1.0 + math.exp(-2.0)
     assert m == 5.0 and abs(l - l_closed) <= TIGHT
-    mo, lo = pa.online_stats(x)
+    (mo, lo), _ = pa.scan(x)
     assert mo == m and abs(lo - l) <= TIGHT
     assert np.allclose(y, [math.exp(-4) / l_closed, 1 / l_closed, math.exp(-2) / l_closed],
                        rtol=0, atol=TIGHT)
@@ -110,22 +110,21 @@ def check_chunk_merge(lib):
     X, widths, g = _chunk_matrix()
     assert sum(widths) == X.shape[1]
     full_row = int(g["fully_masked_row"][0][0])
+    rng = _rng(37)
+    parts = pa.segments(X, widths)                       # every row at once, per segment
+    folded = pa.fold_left(parts)
+    treed = pa.fold_tree(parts)
     for r in range(X.shape[0]):
         _, m, l = oracle.softmax(X[r], lib=lib)
-        # left fold of chunk statistics
-        mf, lf = pa.tile_stats(X[r], widths)
-        # tree ((c0, c1), (c2, c3)), c4
-        cs, pos = [], 0
-        for w in widths:
-            cs.append(pa.chunk_stats(X[r, pos:pos + w]))
-            pos += w
-        left = pa.merge_ml(*pa.merge_ml(*cs[0], *cs[1]), *pa.merge_ml(*cs[2], *cs[3]))
-        mt, lt = pa.merge_ml(*left, *cs[4])
         ref = scipy.special.logsumexp(X[r]) if np.isfinite(X[r]).any() else -np.inf
-        assert mf == m and mt == m
-        assert abs(lf - l) <= TIGHT * max(1.0, l) and abs(lt - l) <= TIGHT * max(1.0, l)
-        assert abs(pa.lse_of(m, l) - ref) <= TIGHT or (ref == -np.inf and pa.lse_of(m, l) == -np.inf)
-        assert not math.isnan(l)
+        row_parts = [(p[0][r], p[1][r]) for p in parts]
+        candidates = [(folded[0][r], folded[1][r]), (treed[0][r], treed[1][r]), pa.scan(X[r])[0]]
+        candidates += [pa.fold_random_tree(row_parts, rng) for _ in range(3)]
+        for mc, lc in candidates:
+            assert mc == m, (r, mc, m)
+            assert abs(lc - l) <= TIGHT * max(1.0, l), (r, lc, l)
+            assert not math.isnan(lc)
+        assert abs(pa.lse((m, l)) - ref) <= TIGHT or (ref == -np.inf and pa.lse((m, l)) == -np.inf)
         if r == full_row:
             assert l == 0.0 and m == -math.inf
     # the same rows through the attention entry: a masked prefix is, up to key
@@ -149,9 +148,9 @@ def check_merge_guard_negative_control(lib):
     # without the guard the fully masked side gives NaN; with it, (m, l) = (-inf, 0)
     _, m, l = oracle.softmax([-np.inf] * 5, lib=lib)
     assert m == -np.inf and l == 0.0
-    _, nl = pa.merge_ml_unguarded(m, l, m, l)
+    _, nl = pa.combine_unguarded((m, l), (m, l))
     assert math.isnan(nl)
-    gm, gl = pa.merge_ml(m, l, m, l)
+    gm, gl = pa.combine((m, l), (m, l))
     assert gm == -np.inf and gl == 0.0
 
 
@@ -166,9 +165,12 @@ def check_tiled_shapes(lib):
         for causal in (False, True):
             for kl in (None, max(Nk - 2, 0), 1):
                 O, L = _attn1(lib, q, k, v, causal=causal, key_lens=None if kl is None else [kl])
-                O1, L1 = pa.flash_v1(q, k, v, Br, Bc, causal=causal, kl=kl)
-                O2, L2 = pa.flash_v2(q, k, v, Br, Bc, causal=causal, kl=kl)
-                for Ot, Lt in ((O1, L1), (O2, L2)):
+                O1, L1 = pa.attention_normalised(q, k, v, Bc, causal=causal, key_len=kl)
+                O2, L2 = pa.attention_deferred(q, k, v, Br, Bc, causal=causal, key_len=kl)
+                # ragged block widths, cycled, for both orders
+                O3, L3 = pa.attention_normalised(q, k, v, [2, 1, 4], causal=causal, key_len=kl)
+                O4, L4 = pa.attention_deferred(q, k, v, [3, 1], [1, 5, 2], causal=causal, key_len=kl)
+                for Ot, Lt in ((O1, L1), (O2, L2), (O3, L3), (O4, L4)):
                     assert np.allclose(O, Ot, rtol=0, atol=TIGHT), (N, Nk, d, causal, kl)
                     fin = np.isfinite(L)
                     assert np.array_equal(fin, np.isfinite(Lt))

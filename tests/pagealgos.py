@@ -1,160 +1,201 @@
-"""Test-side fp64 versions of the streaming algorithms the pages describe.
+"""Test-side fp64 streaming formulations of softmax and attention.
 
-These are independent of the oracle (which is the plain three-pass
-definition): they follow the streaming/tiled forms, so agreement between the
-two pins the oracle to a second formulation, not to itself.
+The oracle computes the plain three-pass definition.  The functions here
+reach the same numbers through the streaming statistics the pages build on,
+so agreement between the two pins the oracle to a second formulation rather
+than to itself.  They are written from the formulas, not from any printed
+program:
 
-  * online_stats:  element-by-element recurrence of running max m and running
-    denominator l ('Online Softmax -- the mathematical heart of
-    FlashAttention' section 2; 'Online softmax in attention -- why and how',
-    section "The online formulation"), skipping while nothing finite has been
-    seen ('Online Softmax & FlashAttention', Step 1).
-  * tile_stats:    the same promoted to tiles with a tile-local max and sum
-    (first page, section 4).
-  * merge_ml:      the associative (m, l) merge with the guard for two -inf
-    sides ('Online Softmax & FlashAttention', Step 1).
-  * flash_v1:      KV-block outer loop, Q-block inner loop, normalised O that is
-    re-scaled and divided at every block ('Online Softmax & FlashAttention',
-    Step 2).
-  * flash_v2:      Q-block outer loop, unnormalised (m, l, o) state per row,
-    one division at the end, LSE returned (its Step 3; first page section 5).
+* A row segment is summarised by the pair (m, l): its max and the sum of
+  exp(x - m) over it ('Online Softmax -- the mathematical heart of
+  FlashAttention', sections 2 and 4; 'Online Softmax & FlashAttention',
+  Step 1).  An empty or fully masked segment is (-inf, 0).
+* Two pairs combine to (M, l1 * w1 + l2 * w2) with M = max(m1, m2) and
+  w_i = exp(m_i - M), where a side that has seen nothing has weight 0 (the
+  guard of Step 1, which keeps -inf - (-inf) out of the arithmetic).  The
+  operation is associative, so a scan, a left fold and any tree of
+  combinations agree.
+* Attention over key blocks carries the pair and an output accumulator per
+  query row and folds each key block in with the combination weights: the
+  accumulator either stays unnormalised and is divided once at the end
+  (research-hub 'Online Softmax' page, "Why it matters"; first page section
+  5), or is kept normalised and re-divided after every block (the V1
+  variant of Step 2).  Blocks may have any widths, and query blocks are
+  independent.
+
+Everything is vectorised with numpy over rows; the only Python loops run
+over blocks or over the pairs being combined.
 """
 from __future__ import annotations
 
-import math
+import functools
+import itertools
 
 import numpy as np
 
 NEG_INF = float("-inf")
 
 
-def online_stats(x, trace=False):
-    m, l = NEG_INF, 0.0
-    ms, ls = [], []
-    for xi in x:
-        m_new = max(m, xi)
-        if m_new == NEG_INF:        # nothing finite yet
-            ms.append(m)
-            ls.append(l)
-            continue
-        l = l * math.exp(m - m_new) + math.exp(xi - m_new)
-        m = m_new
-        ms.append(m)
-        ls.append(l)
-    return (m, l, ms, ls) if trace else (m, l)
+# ----------------------------------------------------------------- (m, l) pairs
+def pair_of(x):
+    """Pair(s) of the segment(s) along the last axis: (max, sum exp(x - max));
+    (-inf, 0) where nothing is finite.  Scalars for 1-D input."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[-1] == 0:
+        shape = x.shape[:-1]
+        return np.full(shape, NEG_INF)[()], np.zeros(shape)[()]
+    m = x.max(axis=-1)
+    empty = np.isneginf(m)
+    shift = np.where(empty, 0.0, m)
+    l = np.where(empty, 0.0, np.exp(x - np.expand_dims(shift, -1)).sum(axis=-1))
+    return m[()], l[()]
 
 
-def chunk_stats(c):
-    """(tile max, tile sum of exp(x - tile max)); (-inf, 0) for an all-masked tile."""
-    c = np.asarray(c, dtype=np.float64)
-    if c.size == 0:
-        return NEG_INF, 0.0
-    m = float(c.max())
-    if m == NEG_INF:
-        return NEG_INF, 0.0
-    return m, float(np.exp(c - m).sum())
-
-
-def merge_ml(m1, l1, m2, l2):
-    m = max(m1, m2)
-    safe = 0.0 if m == NEG_INF else m
-    return m, l1 * math.exp(m1 - safe) + l2 * math.exp(m2 - safe)
-
-
-def merge_ml_unguarded(m1, l1, m2, l2):
-    m = max(m1, m2)
+def combine_weights(m1, m2):
+    """(M, w1, w2): the common max and each side's weight exp(m_i - M), 0 for a
+    side without any finite entry."""
+    m1 = np.asarray(m1, dtype=np.float64)
+    m2 = np.asarray(m2, dtype=np.float64)
+    M = np.maximum(m1, m2)
     with np.errstate(invalid="ignore"):
-        return m, float(np.float64(l1) * np.exp(np.float64(m1) - m)
-                        + np.float64(l2) * np.exp(np.float64(m2) - m))
+        w1 = np.where(np.isneginf(m1), 0.0, np.exp(m1 - M))
+        w2 = np.where(np.isneginf(m2), 0.0, np.exp(m2 - M))
+    return M[()], w1[()], w2[()]
 
 
-def tile_stats(x, widths):
-    """Tile recurrence over consecutive tiles of the given widths."""
-    m, l = NEG_INF, 0.0
-    pos = 0
-    for w in widths:
-        mt, lt = chunk_stats(x[pos:pos + w])
-        m, l = merge_ml(m, l, mt, lt)
-        pos += w
-    return m, l
+def combine(a, b):
+    """a (+) b for pairs a = (m1, l1), b = (m2, l2) (scalars or arrays)."""
+    M, w1, w2 = combine_weights(a[0], b[0])
+    return M, a[1] * w1 + b[1] * w2
 
 
-def lse_of(m, l):
-    return m + math.log(l) if l > 0 else NEG_INF
+def combine_unguarded(a, b):
+    """The same formula with the weights taken as exp(m_i - M) even when both
+    sides are empty (negative control: -inf - (-inf) is NaN)."""
+    M = np.maximum(np.float64(a[0]), np.float64(b[0]))
+    with np.errstate(invalid="ignore"):
+        return M, a[1] * np.exp(np.float64(a[0]) - M) + b[1] * np.exp(np.float64(b[0]) - M)
 
 
-def _visible(N, Nk, causal, kl):
-    vis = np.ones((N, Nk), dtype=bool)
-    if kl is not None:
-        vis[:, min(max(kl, 0), Nk):] = False
+def scan(x):
+    """Single pass over a 1-D row, each element entering as the pair (x_i, 1)
+    (a masked element as (-inf, 0)).  Returns the final pair and the list of
+    running pairs after each element."""
+    singles = [(float(v), 0.0 if v == NEG_INF else 1.0) for v in np.asarray(x, dtype=np.float64)]
+    states = list(itertools.accumulate(singles, combine, initial=(NEG_INF, 0.0)))[1:]
+    final = states[-1] if states else (NEG_INF, 0.0)
+    return (float(final[0]), float(final[1])), [(float(m), float(l)) for m, l in states]
+
+
+def segments(x, widths):
+    """The pairs of consecutive segments of the given widths along the last axis."""
+    edges = np.cumsum([0] + list(widths))
+    return [pair_of(np.asarray(x)[..., a:b]) for a, b in zip(edges[:-1], edges[1:])]
+
+
+def fold_left(pairs):
+    return functools.reduce(combine, pairs, (NEG_INF, 0.0))
+
+
+def fold_tree(pairs):
+    """Balanced tree: combine the two halves' results (lower half first)."""
+    if len(pairs) == 1:
+        return pairs[0]
+    h = len(pairs) // 2
+    return combine(fold_tree(pairs[:h]), fold_tree(pairs[h:]))
+
+
+def fold_random_tree(pairs, rng):
+    """Repeatedly combine a random adjacent couple until one pair is left."""
+    work = list(pairs)
+    while len(work) > 1:
+        i = int(rng.integers(0, len(work) - 1))
+        work[i:i + 2] = [combine(work[i], work[i + 1])]
+    return work[0]
+
+
+def lse(pair):
+    m, l = pair
+    return m + np.log(l) if l > 0 else NEG_INF
+
+
+# ------------------------------------------------------------------ attention
+def visibility(N, Nk, causal=False, key_len=None):
+    """[N, Nk] mask: key j visible to query i (key length, then the causal band
+    j <= i + Nk - N)."""
+    kl = Nk if key_len is None else min(max(key_len, 0), Nk)
+    j = np.arange(Nk)[None, :]
+    vis = np.broadcast_to(j < kl, (N, Nk))
     if causal:
-        i = np.arange(N)[:, None]
-        j = np.arange(Nk)[None, :]
-        vis &= j <= i + (Nk - N)
+        vis = vis & (j <= np.arange(N)[:, None] + (Nk - N))
     return vis
 
 
-def flash_v1(q, k, v, Br=4, Bc=3, scale=None, causal=False, kl=None):
-    """One head: q [N,d], k/v [Nk,d] fp64.  Returns (O, LSE)."""
+def _blocks(total, widths):
+    """Half-open ranges covering [0, total): an int width repeats, a list of
+    widths repeats cyclically."""
+    seq = itertools.cycle([widths] if np.isscalar(widths) else list(widths))
+    a = 0
+    while a < total:
+        b = min(total, a + int(next(seq)))
+        yield a, b
+        a = b
+
+
+def _fold_keys(q, k, v, vis, scale, key_widths, normalised):
+    """Fold every key block into the state of the query rows q (all rows at once)."""
+    n, dv = q.shape[0], v.shape[1]
+    m = np.full(n, NEG_INF)
+    l = np.zeros(n)
+    acc = np.zeros((n, dv))
+    for a, b in _blocks(k.shape[0], key_widths):
+        s = np.where(vis[:, a:b], (q @ k[a:b].T) * scale, NEG_INF)
+        mb, lb = pair_of(s)
+        mb, lb = np.atleast_1d(mb), np.atleast_1d(lb)
+        ref = np.where(np.isneginf(mb), 0.0, mb)
+        pv = np.exp(s - ref[:, None]) @ v[a:b]          # this block's weighted values
+        M, w_old, w_new = combine_weights(m, mb)
+        l_new = l * w_old + lb * w_new
+        if normalised:
+            # acc holds the normalised output so far: undo the old division,
+            # add the block, divide by the new denominator (rows with no key stay 0)
+            num = (l * w_old)[:, None] * acc + w_new[:, None] * pv
+            acc = np.divide(num, l_new[:, None], out=np.zeros_like(num), where=l_new[:, None] > 0)
+        else:
+            acc = w_old[:, None] * acc + w_new[:, None] * pv
+        m, l = np.atleast_1d(M), l_new
+    return m, l, acc
+
+
+def attention_deferred(q, k, v, query_widths=4, key_widths=3, scale=None, causal=False, key_len=None):
+    """One head, query blocks independent of each other; within a block the key
+    blocks are folded into unnormalised (m, l, acc), divided once at the end.
+    Returns (O, LSE); rows without a visible key give O = 0, LSE = -inf."""
     N, d = q.shape
-    Nk = k.shape[0]
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
-    vis = _visible(N, Nk, causal, kl)
-    O = np.zeros((N, d))
-    l = np.zeros(N)
-    m = np.full(N, NEG_INF)
-    for j0 in range(0, Nk, Bc):                   # outer: one KV block
-        Kj, Vj = k[j0:j0 + Bc], v[j0:j0 + Bc]
-        for i0 in range(0, N, Br):                # inner: every Q block
-            S = q[i0:i0 + Br] @ Kj.T * scale
-            S = np.where(vis[i0:i0 + Br, j0:j0 + Bc], S, NEG_INF)
-            for r in range(S.shape[0]):
-                i = i0 + r
-                m_ij, l_ij = chunk_stats(S[r])
-                if m_ij == NEG_INF:
-                    continue
-                P = np.exp(S[r] - m_ij)
-                m_new, l_new = merge_ml(m[i], l[i], m_ij, l_ij)
-                a_old = l[i] * math.exp(m[i] - m_new) if l[i] > 0 else 0.0
-                O[i] = (a_old * O[i] + math.exp(m_ij - m_new) * (P @ Vj)) / l_new
-                m[i], l[i] = m_new, l_new
-    lse = np.array([lse_of(m[i], l[i]) for i in range(N)])
-    return O, lse
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    vis = visibility(N, k.shape[0], causal, key_len)
+    O = np.zeros((N, v.shape[1]))
+    L = np.full(N, NEG_INF)
+    for a, b in _blocks(N, query_widths):
+        m, l, acc = _fold_keys(q[a:b], k, v, vis[a:b], scale, key_widths, normalised=False)
+        seen = l > 0
+        O[a:b][seen] = acc[seen] / l[seen, None]
+        L[a:b][seen] = m[seen] + np.log(l[seen])
+    return O, L
 
 
-def flash_v2(q, k, v, Br=4, Bc=3, scale=None, causal=False, kl=None):
-    """One head, Q-block outer / KV inner, unnormalised o, one divide at the end."""
+def attention_normalised(q, k, v, key_widths=3, scale=None, causal=False, key_len=None):
+    """One head, key blocks outermost over all query rows, the output kept
+    normalised after every block.  Returns (O, LSE)."""
     N, d = q.shape
-    Nk = k.shape[0]
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
-    vis = _visible(N, Nk, causal, kl)
-    O = np.zeros((N, d))
-    LSE = np.full(N, NEG_INF)
-    for i0 in range(0, N, Br):
-        rows = range(i0, min(i0 + Br, N))
-        m = {i: NEG_INF for i in rows}
-        l = {i: 0.0 for i in rows}
-        o = {i: np.zeros(d) for i in rows}
-        for j0 in range(0, Nk, Bc):
-            Kj, Vj = k[j0:j0 + Bc], v[j0:j0 + Bc]
-            for i in rows:
-                s = (Kj @ q[i]) * scale
-                s = np.where(vis[i, j0:j0 + Bc], s, NEG_INF)
-                m_new = max(m[i], float(s.max()))
-                if m_new == NEG_INF:
-                    continue
-                alpha = math.exp(m[i] - m_new)
-                beta = np.exp(s - m_new)
-                l[i] = alpha * l[i] + beta.sum()
-                o[i] = alpha * o[i] + beta @ Vj
-                m[i] = m_new
-        for i in rows:
-            if l[i] > 0:
-                O[i] = o[i] / l[i]
-                LSE[i] = m[i] + math.log(l[i])
-    return O, LSE
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    vis = visibility(N, k.shape[0], causal, key_len)
+    m, l, O = _fold_keys(q, k, v, vis, scale, key_widths, normalised=True)
+    L = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return O, L
 
 
+# ------------------------------------------------------------------ fixtures
 def read_golden(path):
     """key -> list of tokens, from a '#'-commented whitespace fixture."""
     out = {}

@@ -26,15 +26,15 @@ def test_online_trace_matches_printed_example():
     g = pa.read_golden(oc.os.path.join(oc.GOLDEN, "softmax_worked_example.txt"))
     tol = 0.5 * 10 ** (-int(g["decimals"][0][0])) + 1e-12
     x = [float(t) for t in g["x"][0]]
-    m, l, ms, ls = pa.online_stats(x, trace=True)
-    assert ms == [float(t) for t in g["online_m"][0]]
-    assert all(abs(a - float(b)) <= tol for a, b in zip(ls, g["online_d"][0]))
+    _, states = pa.scan(x)
+    assert [s[0] for s in states] == [float(t) for t in g["online_m"][0]]
+    assert all(abs(s[1] - float(b)) <= tol for s, b in zip(states, g["online_d"][0]))
 
 
 def test_tile_recurrence_equals_scalar():
     # four elements in two tiles of two, as the first page suggests
     x = [1.0, 3.0, 2.0, 5.0]
-    m1, l1 = pa.online_stats(x)
-    m2, l2 = pa.tile_stats(x, [2, 2])
+    (m1, l1), _ = pa.scan(x)
+    m2, l2 = pa.fold_left(pa.segments(x, [2, 2]))
     assert m1 == m2 and abs(l1 - l2) <= 1e-15
-    assert abs(pa.lse_of(m1, l1) - (5 + math.log(l1))) == 0
+    assert abs(pa.lse((m1, l1)) - (5 + math.log(l1))) == 0
