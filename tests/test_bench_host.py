@@ -30,6 +30,16 @@ def test_prefill_flops():
     assert bench.prefill_flops(w, [-5, 10 ** 9]) == 4 * 8 * 4096 * 128 * 4096
 
 
+def test_prefill_bytes():
+    # Q, K, V read once and O written (bf16), LSE written (fp32)
+    w = WORKLOADS["causal_bf16_b1h32_n8192_d128"]
+    assert bench.prefill_bytes(w) == 4 * 32 * 8192 * 128 * 2 + 32 * 8192 * 4
+    # key lengths: only the visible K/V rows; a batch without keys reads no Q
+    w = WORKLOADS["masked_bf16_b2h8_n4096_d128"]
+    q_o = 2 * 8 * 4096 * 128 * 2 * 2 - 8 * 4096 * 128 * 2
+    assert bench.prefill_bytes(w, [1013, 0]) == q_o + 2 * 8 * 1013 * 128 * 2 + 2 * 8 * 4096 * 4
+
+
 def test_decode_bytes():
     # K and V read once, Q read, O and LSE written
     w = WORKLOADS["decode_bf16_b64h32_nk16384_d128"]
@@ -63,6 +73,12 @@ def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     f.write_text(text.replace("kUnroll = 16", "kUnroll = 8", 1))
     assert "kUnroll = 16" in text
     assert _hash_of(tmp_path, monkeypatch) != h0          # a code change: different
+    # a record naming its own sources ignores changes to the others
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    fwd = bench.kernel_source_hash(bench.SOURCES_FWD)
+    f.write_text(text)
+    assert bench.kernel_source_hash(bench.SOURCES_FWD) == fwd
+    assert bench.kernel_source_hash(bench.SOURCES_DECODE) != bench.kernel_source_hash(bench.SOURCES_FWD)
 
 
 def test_bench_refuses_more_than_one_gpu():
