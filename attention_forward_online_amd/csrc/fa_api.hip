@@ -67,6 +67,7 @@ const char *fa_status_str(fa_status status) {
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
         case FA_ERR_HIP: return "FA_ERR_HIP";
+        case FA_ERR_SCRATCH_LIMIT: return "FA_ERR_SCRATCH_LIMIT";
     }
     return "FA_ERR_UNKNOWN";
 }
@@ -108,10 +109,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits) {
     return (size_t)B * (size_t)H * (size_t)num_splits * ((size_t)d + 2) * sizeof(float);
 }
 
-fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                            int B, int H, int Nk, int d, float scale, const int32_t *key_lens,
-                            int num_splits, void *workspace, size_t workspace_bytes,
-                            fa_dtype dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode entry points (everything but the workspace).
+fa_status check_decode(const void *Q, const void *K, const void *V, void *O, float *LSE, int B,
+                       int H, int Nk, int d, float scale, const int32_t *key_lens, int num_splits,
+                       fa_dtype dtype) {
     if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
     if (B < 0 || H < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
     if (num_splits < 1) return FA_ERR_INVALID_ARG;
@@ -123,16 +128,48 @@ fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O
     if ((long long)B * H * (long long)Nk * d > kMaxElems) return FA_ERR_INVALID_ARG;
     if ((long long)Nk * d * (dtype == FA_BF16 ? 2 : 4) > kMaxSliceBytes) return FA_ERR_INVALID_ARG;
     if (B > kMaxGridYZ || H > kMaxGridYZ || (long long)B * H > kMaxGridX) return FA_ERR_INVALID_ARG;
-    if (!Q || !O || !LSE || !workspace) return FA_ERR_INVALID_ARG;
+    if (!Q || !O || !LSE) return FA_ERR_INVALID_ARG;
     if (Nk > 0 && (!K || !V)) return FA_ERR_INVALID_ARG;
-    if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE) || !aligned16(workspace))
-        return FA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || !aligned4(LSE)) return FA_ERR_INVALID_ARG;
     if (Nk > 0 && (!aligned16(K) || !aligned16(V))) return FA_ERR_INVALID_ARG;
     if (key_lens && !aligned4(key_lens)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                            int B, int H, int Nk, int d, float scale, const int32_t *key_lens,
+                            int num_splits, void *workspace, size_t workspace_bytes,
+                            fa_dtype dtype, void *stream) {
+    const fa_status st = check_decode(Q, K, V, O, LSE, B, H, Nk, d, scale, key_lens, num_splits, dtype);
+    if (st != FA_OK || (long long)B * H == 0) return st;
+    if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
     if (workspace_bytes < fa_decode_workspace_bytes(B, H, d, num_splits)) return FA_ERR_INVALID_ARG;
 
     fa::DecodeArgs a{Q, K, V, O, LSE, key_lens, B, H, Nk, d, scale, num_splits,
                      static_cast<float *>(workspace)};
+    return from_hip(fa::launch_decode(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_decode_scratch_bytes(void) { return fa::kDecodeScratchBytes; }
+
+fa_status fa_decode_splitkv_noalloc(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                                    int B, int H, int Nk, int d, float scale,
+                                    const int32_t *key_lens, int num_splits, fa_dtype dtype,
+                                    void *stream) {
+    const fa_status st = check_decode(Q, K, V, O, LSE, B, H, Nk, d, scale, key_lens, num_splits, dtype);
+    if (st != FA_OK || (long long)B * H == 0) return st;
+    // sizes are checked before the device is touched
+    if (fa_decode_workspace_bytes(B, H, d, num_splits) > fa::kDecodeScratchBytes)
+        return FA_ERR_SCRATCH_LIMIT;
+    void *scr = nullptr;
+    const hipError_t e = fa::decode_scratch(&scr);
+    if (e != hipSuccess) return from_hip(e);
+    fa::DecodeArgs a{Q, K, V, O, LSE, key_lens, B, H, Nk, d, scale, num_splits,
+                     static_cast<float *>(scr)};
     return from_hip(fa::launch_decode(a, dtype == FA_BF16, static_cast<hipStream_t>(stream)));
 }
 

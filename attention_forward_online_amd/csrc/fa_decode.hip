@@ -22,11 +22,48 @@
 // the same (m, l) merge before the chunk's partial is written.
 //
 // Workspace layout (fp32): o[B][H][S][d], then m[B][H][S], then l[B][H][S];
-// m is stored as scale*log2(e)*max score (-inf for an empty chunk).
+// m is stored as scale*log2(e)*max score (-inf for an empty chunk).  The split
+// kernel writes every record, empty chunks included, before the combine reads
+// them, so the workspace needs no clearing between calls.
+//
+// For callers that cannot allocate, the library also holds one fixed scratch
+// array per GPU (`scratch` below, kDecodeScratchBytes) that can stand in for
+// the caller's workspace.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
+
+// Partial states of the decode entry point that allocates nothing.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code this name is only a handle: the device address comes from
+// hipGetSymbolAddress (decode_scratch below).
+__device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+// Device address of this GPU's `scratch`, looked up once per device (with that
+// device current) and kept; a failed lookup is returned and retried next call.
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = 256;

@@ -58,6 +58,10 @@ int device_cu_count();
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 // split-KV decode, d in {64, 128}; is_bf16 selects the element type.
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
+// The decode's fixed per-GPU scratch (used in place of a caller workspace):
+// its size, and its device address on the current GPU.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void **ptr);
 
 // Row softmax / log-sum-exp of a [rows, cols] fp32 or bf16 matrix.
 size_t softmax_workspace_bytes(long long rows, long long cols, bool is_bf16);

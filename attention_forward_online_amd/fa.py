@@ -16,11 +16,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 FA_F32, FA_BF16 = 0, 1
 
 #: every symbol include/fa.h declares
 EXPORTS = ("fa_forward", "fa_decode_workspace_bytes", "fa_decode_splitkv",
+           "fa_decode_splitkv_noalloc", "fa_decode_scratch_bytes",
            "fa_softmax_workspace_bytes", "fa_softmax", "fa_forward_v1_workspace_bytes",
            "fa_forward_v1", "fa_backward_workspace_bytes", "fa_backward",
            "fa_status_str", "fa_last_hip_error")
@@ -51,6 +52,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, i, vp, sz, i, vp]
     lib.fa_decode_splitkv.restype = i
+    lib.fa_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp, i, i, vp]
+    lib.fa_decode_splitkv_noalloc.restype = i
+    lib.fa_decode_scratch_bytes.argtypes = []
+    lib.fa_decode_scratch_bytes.restype = sz
     i64 = ctypes.c_int64
     lib.fa_softmax_workspace_bytes.argtypes = [i64, i64, i]
     lib.fa_softmax_workspace_bytes.restype = sz
@@ -168,6 +173,22 @@ def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(load_library().fa_decode_workspace_bytes(B, H, d, num_splits))
 
 
+def _decode_shapes(q, k, v, o, lse, key_lens, idx):
+    for n, t in (("k", k), ("v", v), ("o", o)):
+        _check_dev(n, t, q.dtype, idx)
+    _check_dev("lse", lse, torch.float32, idx)
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    if N != 1 or k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
+            or lse.shape != (B, H, 1):
+        raise ValueError("decode expects q, o [B,H,1,d], k, v [B,H,Nk,d], lse [B,H,1]")
+    if key_lens is not None:
+        _check_dev("key_lens", key_lens, torch.int32, idx)
+        if key_lens.shape != (B,):
+            raise ValueError("key_lens must have shape [B]")
+    return B, H, Nk, d
+
+
 def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       lse: torch.Tensor, num_splits: int, workspace: torch.Tensor,
                       scale: Optional[float] = None, key_lens: Optional[torch.Tensor] = None,
@@ -180,19 +201,8 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     lib = _lib or load_library()
     _check_dev("q", q)
     idx = q.get_device()
-    for n, t in (("k", k), ("v", v), ("o", o)):
-        _check_dev(n, t, q.dtype, idx)
-    _check_dev("lse", lse, torch.float32, idx)
+    B, H, Nk, d = _decode_shapes(q, k, v, o, lse, key_lens, idx)
     _check_dev("workspace", workspace, None, idx)
-    B, H, N, d = q.shape
-    Nk = k.shape[2]
-    if N != 1 or k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d) or o.shape != q.shape \
-            or lse.shape != (B, H, 1):
-        raise ValueError("decode expects q, o [B,H,1,d], k, v [B,H,Nk,d], lse [B,H,1]")
-    if key_lens is not None:
-        _check_dev("key_lens", key_lens, torch.int32, idx)
-        if key_lens.shape != (B,):
-            raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -201,6 +211,30 @@ def fa_decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
         _ptr(key_lens), int(num_splits), _ptr(workspace), ws_bytes, _dtype_code(q), h))
     if st != FA_OK:
         raise FaError(st, "fa_decode_splitkv",
+                      lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_decode_scratch_bytes() -> int:
+    return int(load_library().fa_decode_scratch_bytes())
+
+
+def fa_decode_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                              lse: torch.Tensor, num_splits: int, scale: Optional[float] = None,
+                              key_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The same decode through fa_decode_splitkv_noalloc: no workspace argument,
+    the partials go to the library's fixed per-GPU scratch (nothing is
+    allocated).  Calls that overlap in time on one GPU race."""
+    lib = _lib or load_library()
+    _check_dev("q", q)
+    idx = q.get_device()
+    B, H, Nk, d = _decode_shapes(q, k, v, o, lse, key_lens, idx)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    st = _launch(idx, stream, lambda h: lib.fa_decode_splitkv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nk, d, float(scale),
+        _ptr(key_lens), int(num_splits), _dtype_code(q), h))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_splitkv_noalloc",
                       lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
 
 

@@ -45,7 +45,9 @@ typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, negative size, bad flag, too-small workspace */
     FA_ERR_UNSUPPORTED = 2,   /* valid request this build has no kernel for (e.g. bf16 with d = 96) */
-    FA_ERR_HIP = 3            /* the HIP runtime reported an error at launch */
+    FA_ERR_HIP = 3,           /* the HIP runtime reported an error at launch */
+    FA_ERR_SCRATCH_LIMIT = 4  /* the request needs more than the library's fixed scratch
+                                 (fa_decode_splitkv_noalloc only) */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -106,6 +108,31 @@ fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O
                             const int32_t *key_lens, int num_splits,
                             void *workspace, size_t workspace_bytes,
                             fa_dtype dtype, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as fa_decode_splitkv, same arguments minus the workspace, with the
+ * partial states kept in a fixed scratch array that the library holds on each
+ * GPU it runs on until the process ends (fa_decode_scratch_bytes() bytes,
+ * 32 MiB).  This call allocates nothing.
+ *   Requests needing more than that (fa_decode_workspace_bytes(B, H, d,
+ *   num_splits) > fa_decode_scratch_bytes()) return FA_ERR_SCRATCH_LIMIT
+ *   before anything is launched; the other argument checks and supported
+ *   cases are those of fa_decode_splitkv.  Every record of the scratch that a
+ *   call reads is first written by that call (nothing needs to start at
+ *   zero), and the array keeps the last call's partials afterwards.
+ *   All calls on one GPU share that GPU's array: two calls that overlap in
+ *   time on the same GPU (different streams, not synchronised) race and give
+ *   undefined results.  Calls on different GPUs are independent.
+ */
+fa_status fa_decode_splitkv_noalloc(const void *Q, const void *K, const void *V, void *O,
+                                    float *LSE, int B, int H, int Nk, int d, float scale,
+                                    const int32_t *key_lens, int num_splits, fa_dtype dtype,
+                                    void *stream);
+
+/* Size in bytes of the fixed per-GPU scratch fa_decode_splitkv_noalloc uses. */
+size_t fa_decode_scratch_bytes(void);
 
 /*
  * Bytes of device workspace fa_softmax needs for a [rows, cols] matrix of

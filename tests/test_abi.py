@@ -138,6 +138,33 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == fa.FA_OK
 
 
+def dec_na(lib, Q=P, K=P, V=P, O=P, LSE=P, B=2, H=2, Nk=64, d=128, scale=0.1, key_lens=None,
+           S=4, dtype=fa.FA_BF16):
+    return lib.fa_decode_splitkv_noalloc(Q, K, V, O, LSE, B, H, Nk, d, scale, key_lens, S, dtype, None)
+
+
+def test_decode_noalloc_checks_before_any_launch(lib):
+    # the scratch limit and every argument check answer on the host, before the
+    # device is touched (no GPU here)
+    limit = lib.fa_decode_scratch_bytes()
+    assert limit == 32 << 20
+    # the decode workload (B=64, H=32, d=128, 16 splits: 17.0 MB) fits
+    assert lib.fa_decode_workspace_bytes(64, 32, 128, 16) <= limit
+    # one more split per head than fits
+    S = 64
+    B = limit // (32 * S * (128 + 2) * 4) + 1
+    assert lib.fa_decode_workspace_bytes(B, 32, 128, S) > limit
+    assert dec_na(lib, B=B, H=32, S=S) == fa.FA_ERR_SCRATCH_LIMIT
+    assert fa.status_str(fa.FA_ERR_SCRATCH_LIMIT) == "FA_ERR_SCRATCH_LIMIT"
+    bad, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    assert dec_na(lib, dtype=3) == bad and dec_na(lib, S=0) == bad
+    assert dec_na(lib, Q=None) == bad and dec_na(lib, K=None) == bad and dec_na(lib, LSE=None) == bad
+    assert dec_na(lib, Q=P + 4) == bad and dec_na(lib, Nk=-1) == bad
+    assert dec_na(lib, scale=float("nan")) == bad
+    assert dec_na(lib, d=96) == uns and dec_na(lib, S=257) == uns and dec_na(lib, scale=0.0) == uns
+    assert dec_na(lib, Q=None, K=None, V=None, O=None, LSE=None, B=0) == fa.FA_OK
+
+
 def wsz(rows, chunks):
     return 16 + rows * chunks * 8
 
