@@ -269,4 +269,6 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
 
 void fa_testing_set_softmax_spin_limit(int limit) { fa::set_softmax_spin_limit(limit); }
 
+void fa_testing_set_rescale_rule(int rule) { fa::set_rescale_rule(rule); }
+
 }  // extern "C"

@@ -34,16 +34,24 @@
 //   * Scores stay fp32; exp runs as 2^(s*scale*log2 e - m'), one FMA plus
 //     v_exp_f32 per score; P is rounded to bf16 (RNE) only as the MFMA operand
 //     while the row sum uses the fp32 values.
-//   * Lazy rescale: the reference max moves only when a tile's max exceeds it
-//     by more than 8 in log2 units, i.e. a weight would pass 2^8 (FA-4's
-//     thresholded rescale); o and l always share the
-//     reference, so the result is unchanged while most tiles skip the
-//     rescale of the accumulators.
+//   * Conditional rescale (FA-4 on the research-hub 'Online Softmax' page,
+//     "Why it matters": rescale only when the max shift threatens stability).
+//     o and l always share one reference m', so o / l and m' + log2 l are
+//     exact whatever m' is, as long as no weight 2^(s - m') overflows.  The
+//     default rule (overflow guard) therefore takes no per-tile row max: each
+//     group of weights is made against the current m', and only when some
+//     lane's sum of a group reaches 2^32 (or a lane has no m' yet) is the
+//     group's max taken, m' moved to it, o and l rescaled and the group made
+//     again.  The first tile's max is always taken.  Two ablation rules keep
+//     the per-tile max: the threshold rule (m' moves when the max grows by
+//     more than 8 in log2 units) and the eager rule (every tile, the plain
+//     recurrence).
 //   * Software pipeline within each wave: iteration t issues the MFMAs of
 //     S(t+1) = K(t+1) Q^T with the exponentials of tile t between them, then
-//     the MFMAs of O += P(t) V(t) with the rest of those exponentials and the
-//     row max of tile t+1 between them, so the matrix pipe and the vector ALUs
-//     of one wave work at the same time.  Scheduling barriers fix the order of
+//     the MFMAs of O += P(t) V(t) with the rest of those exponentials (and,
+//     under the ablation rules, the row max of tile t+1) between them, so the
+//     matrix pipe and the vector ALUs of one wave work at the same time.  The
+//     guard checks each group of weights before the first MFMA that uses it.  Scheduling barriers fix the order of
 //     each MFMA and its VALU group; pin() keeps the compiler from sinking the
 //     VALU work towards its later uses.  The loop is unrolled by two so that
 //     S(t) and S(t+1) alternate between two register sets without copies.
@@ -63,6 +71,8 @@
 //     the longest blocks; all blocks of a head run on one XCD (the dispatcher
 //     deals workgroup ids to the 8 XCDs round-robin), so K/V re-reads of a
 //     head hit one L2, and consecutive heads go to different XCDs.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -81,7 +91,12 @@ constexpr int kBc = 64;                     // keys per K/V tile
 // disjoint bank ranges.
 constexpr int kPadK = 8;
 constexpr int kPadV = 32;
-constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale
+constexpr float kLazyTau = 8.0f;            // log2 growth allowed before a rescale (threshold rule)
+// Overflow-guard rule: a tile's weights, taken against the current reference,
+// are kept when every lane's sum of them stays below 2^32 (so every weight is
+// below 2^32 and, over at most 2^31 keys, l stays below 2^63: far inside fp32);
+// otherwise the tile's max is taken and the reference moves to it.
+constexpr float kGuardLimit = 4294967296.0f;
 constexpr int kPrefetch = 2;                // LDS operands read this many MFMAs ahead
 
 template <int N_> struct IntC { static constexpr int value = N_; };
@@ -90,7 +105,7 @@ template <bool B_> struct BoolC { static constexpr bool value = B_; };
 // d = 64 fits three waves per SIMD (<= 168 VGPRs), d = 128 two.  KSPLIT = 2:
 // two groups of four waves share each query block, group g taking the g-th
 // half of its key tiles; their states are merged at the end.
-template <int D, bool CAUSAL, int KSPLIT>
+template <int D, bool CAUSAL, int KSPLIT, int RULE>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 2)) void fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
@@ -101,6 +116,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     static_assert((KS / 2) % 8 == 4 && (VS / 2) % 32 == 16, "LDS strides off the bank pattern");
     constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
     constexpr int CB = D / 32;                  // 32-column blocks of O^T
+    constexpr bool GUARD = RULE == kRuleGuard;
     constexpr int NS = 2 * KK;                  // S MFMAs per tile (= P pairs made beside them)
     constexpr int NP2 = 4 * CB;                 // P.V MFMAs per tile
     constexpr int PAIRS2 = 16 - NS;             // P pairs left for the P.V section
@@ -110,6 +126,10 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     // choice neutral)
     constexpr int kPrioPhase = D == 64 ? 2 : 1;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
+    // the guard checks the pairs made beside the P.V MFMAs before the MFMAs
+    // that use them: all of them are made beside the first half
+    static_assert(PAIRS2 == 0 || (PAIRS2 / 2 == NP2 / 2 && NS / 4 == NP2 / (2 * CB)),
+                  "guard: second pair group must end half way through P.V");
     static_assert(KSPLIT >= 1 && KSPLIT <= 3, "one to three key groups");
 
     // one array per stage, so that the stage a load fills and the stage the
@@ -193,6 +213,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     float ms = neg_inf();
     float ref = 0.f;        // the reference the next probabilities use (0 while ms = -inf)
     float l = 0.f;          // this lane's half of the running denominator
+    bool all_ref = false;   // guard rule: every lane of the wave has a finite reference
 
     // K/V tiles go from HBM straight into LDS (16-byte buffer loads with the
     // LDS flag: lane l of a wave's load fills bytes 16 l .. 16 l + 15 of a 1 KiB
@@ -229,16 +250,20 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     };
     auto dma_k = [&](uint16_t *dst, int t) { dma(IntC<NJK>{}, goffk, K + kv_base, dst, t); };
     auto dma_v = [&](uint16_t *dst, int t) { dma(IntC<NJV>{}, goffv, V + kv_base, dst, t); };
+    // Each lane's element offsets within a K and a V stage, computed once: the
+    // operands below add only compile-time offsets to them.
+    const int k_lane = krow * KS + 8 * g;
+    const int v_lane = (8 * g + vrow) * VS + vcol;
     // operand of S MFMA i (block jb = i % 2, k-step kk = i / 2) from the K tile in `stage`
     auto k_operand = [&](int stage, int i) {
         const int jb = i & 1, kk = i >> 1;
-        return *(const u32x4_t *)&kst(stage)[(32 * jb + krow) * KS + 8 * g + 16 * kk];
+        return *(const u32x4_t *)&kst(stage)[k_lane + 32 * jb * KS + 16 * kk];
     };
     // operand of P.V MFMA i (chunk ci = i / CB = 2 jb + h, column block cb = i % CB)
     auto v_operand = [&](int stage, int i) {
         const int ci = i / CB, cb = i % CB, jb = ci >> 1, h = ci & 1;
-        const auto *p0 = (const __attribute__((address_space(3))) uint16_t *)vst(stage) +
-                         (8 * g + vrow + 32 * jb + 16 * h) * VS + vcol + 32 * cb;
+        const auto *p0 = (const __attribute__((address_space(3))) uint16_t *)vst(stage) + v_lane +
+                         (32 * jb + 16 * h) * VS + 32 * cb;
         const u32x2_t lo = lds_read_tr16(p0);
         const u32x2_t hi = lds_read_tr16(p0 + 4 * VS);
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
@@ -274,19 +299,38 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
             for (int v = 0; v < 16; ++v)
                 if (32 * jb + 16 * (v >> 3) + (v & 7) >= lim) sc[jb][v] = neg_inf();
     };
-    // lazy move of the reference after a tile's row max mx (log2 units)
+    // move of the reference after a tile's row max mx (log2 units).  Eager:
+    // every tile, m' = max(m', mx) and o, l *= 2^(m'_old - m') (the plain
+    // recurrence).  Threshold: only lanes whose max grew by more than kLazyTau
+    // move, and the accumulators are touched only when some lane of the wave
+    // moves.  Guard: called on the slow path only, any growth moves.
+    // Returns the factor o and l were scaled by (1 when nothing moved).
     auto decide = [&](float mx) {
-        const bool move = mx > ms + kLazyTau;   // false for a fully masked tile
-        if (__any(move)) {
-            const float alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
+        float alpha = 1.f;
+        if constexpr (RULE == kRuleEager) {
+            const float mn = fmaxf(ms, mx);
+            alpha = mn == neg_inf() ? 1.f : exp2_hw(ms - mn);   // 0 when ms = -inf
             l *= alpha;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
-            ms = move ? mx : ms;
+            ms = mn;
+        } else {
+            const bool move = mx > ms + (RULE == kRuleTau ? kLazyTau : 0.f);   // false for a fully masked tile
+            if (__any(move)) {
+                alpha = move ? exp2_hw(ms - mx) : 1.f;   // 0 when ms = -inf
+                l *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[cb][v] *= alpha;
+                ms = move ? mx : ms;
+            }
         }
         ref = ms == neg_inf() ? 0.f : ms;
+        if constexpr (GUARD) all_ref = !__any(ms == neg_inf());
+        return alpha;
     };
     auto rowmax = [&](const float (&m4)[4]) {
         return max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
@@ -335,6 +379,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         constexpr bool LAST = decltype(last_c)::value;
         refill(par, t);
         uint32_t pk[4][4];
+        // row-sum partials of the pairs being made: those beside the S MFMAs,
+        // then (folded into ts first) those beside the P.V MFMAs
         float rs[4] = {-0.f, -0.f, -0.f, -0.f};
         // last tile: keys 32..63 of it all past the wave's visible keys?
         bool half = false;
@@ -343,6 +389,25 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
             const int vis_last = CAUSAL ? min(kv_lim - 1, wq_last + off) : kv_lim - 1;
             half = j0 + 32 > vis_last;
         }
+        // Guard rule, slow path for pairs [q0, q1) (whole chunks of 4 pairs):
+        // the max of their scores, the reference moved to it where it grew
+        // (o and l, which hold everything before these pairs, rescaled), the
+        // pairs made again into r.  A reference that covers the pairs being
+        // made is all the recurrence needs: pairs made later are checked
+        // again.  Returns the rescale factor.
+        [[maybe_unused]] auto redo = [&](auto q0_c, auto q1_c, float (&r)[4]) {
+            constexpr int q0 = decltype(q0_c)::value, q1 = decltype(q1_c)::value;
+            float mx = neg_inf();
+#pragma unroll
+            for (int k = q0 / 4; k < q1 / 4; ++k) mx = fmaxf(mx, max8(sc, k));
+            const float alpha = decide(max_xor32(mx) * c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[k] = -0.f;
+#pragma unroll
+            for (int q = q0; q < q1; ++q)
+                if (!LAST || !half || q < 8) p_pair(sc, q, pk, r);
+            return alpha;
+        };
         u32x4_t kop[PD];
         if constexpr (!LAST) {
 #pragma unroll
@@ -361,7 +426,20 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (!LAST)
             if (need_mask(t + 1)) apply_mask(t + 1, sn);
-        float m4[4];
+        // Guard rule: the weights made so far (pairs 0 .. NS-1) are kept unless
+        // some lane's sum of them reached the limit or a lane has no reference
+        // yet; the pairs made beside the P.V MFMAs are checked the same way
+        // before the MFMAs that use them.
+        float ts = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        if constexpr (GUARD) {
+            if (!all_ref || __any(!(ts < kGuardLimit))) {
+                redo(IntC<0>{}, IntC<NS>{}, rs);
+                ts = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rs[k] = -0.f;
+        [[maybe_unused]] float m4[4];
         u32x4_t vop[PD];
 #pragma unroll
         for (int i = 0; i < PD; ++i) vop[i] = v_operand(par, i);
@@ -369,6 +447,13 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
 #pragma unroll
         for (int i = 0; i < NP2; ++i) {
             const int ci = i / CB;
+            if constexpr (GUARD && PAIRS2 > 0) {
+                if (i == NP2 / 2 && (!LAST || !half)) {
+                    const float ts2 = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+                    if (__any(!(ts2 < kGuardLimit)))
+                        ts *= redo(IntC<NS>{}, IntC<16>{}, rs);   // the first pairs are in o already
+                }
+            }
             if (!LAST || !half || ci < 2)
                 acc[i % CB] = mfma32(vop[i % PD], u32x4_t{pk[ci][0], pk[ci][1], pk[ci][2], pk[ci][3]},
                                      acc[i % CB]);
@@ -377,7 +462,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
                 p_pair(sc, NS + 2 * i, pk, rs);
                 p_pair(sc, NS + 2 * i + 1, pk, rs);
             }
-            if constexpr (!LAST) {
+            if constexpr (!LAST && !GUARD) {
                 if (i >= NP2 - 4) {
                     m4[i - (NP2 - 4)] = max8(sn, i - (NP2 - 4));
                     pin(m4[i - (NP2 - 4)]);
@@ -386,8 +471,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (kPrioPhase == 2) __builtin_amdgcn_s_setprio(0);
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        if constexpr (!LAST) decide(rowmax(m4));
+        l += ts + ((rs[0] + rs[1]) + (rs[2] + rs[3]));
+        if constexpr (!GUARD && !LAST) decide(rowmax(m4));
         wait_vmem_all();
         __syncthreads();
     };
@@ -470,10 +555,10 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
 }
 
 
-template <int D, bool CAUSAL, int KSPLIT>
+template <int D, bool CAUSAL, int KSPLIT, int RULE>
 hipError_t launch_one(const FwdArgs &a, int n_qtiles, long long nblocks, int order,
                       hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, KSPLIT>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, KSPLIT, RULE>), dim3((unsigned)nblocks),
                        dim3(kThreads * KSPLIT), 0, stream, (const uint16_t *)a.Q,
                        (const uint16_t *)a.K, (const uint16_t *)a.V, (uint16_t *)a.O, a.LSE,
                        a.key_lens, a.H, a.N, a.Nk, n_qtiles, order, a.scale * kLog2e);
@@ -491,12 +576,25 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     // of four waves instead.  Such a workgroup needs the LDS of two and runs
     // one per CU, so with more blocks than CUs it would take more dispatch
     // rounds than the unsplit grid (measured slower at 512 blocks).
+    // rescale rules other than the default exist for the ablation only and
+    // always run unsplit
+    const int rule = rescale_rule();
+    if (rule == kRuleEager) return launch_one<D, CAUSAL, 1, kRuleEager>(a, n_qtiles, nblocks, order, stream);
+    if (rule == kRuleTau) return launch_one<D, CAUSAL, 1, kRuleTau>(a, n_qtiles, nblocks, order, stream);
     if (nblocks <= device_cu_count())
-        return launch_one<D, CAUSAL, 2>(a, n_qtiles, nblocks, order, stream);
-    return launch_one<D, CAUSAL, 1>(a, n_qtiles, nblocks, order, stream);
+        return launch_one<D, CAUSAL, 2, kRuleGuard>(a, n_qtiles, nblocks, order, stream);
+    return launch_one<D, CAUSAL, 1, kRuleGuard>(a, n_qtiles, nblocks, order, stream);
 }
 
 }  // namespace
+
+namespace {
+std::atomic<int> g_rescale_rule{kRuleGuard};
+}  // namespace
+void set_rescale_rule(int rule) {
+    g_rescale_rule.store(rule == kRuleEager || rule == kRuleTau ? rule : kRuleGuard);
+}
+int rescale_rule() { return g_rescale_rule.load(std::memory_order_relaxed); }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
     if (a.d == 64) return a.causal ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);

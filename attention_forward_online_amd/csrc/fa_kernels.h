@@ -77,5 +77,10 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t stream);
 // Test hook: polls of the one-pass wait before its fallback (< 0: default).
 void set_softmax_spin_limit(int limit);
+// Rescale rule of the bf16 prefill: the overflow guard (default), the FA-4
+// threshold or the eager per-tile rescale.  Test and ablation hook.
+constexpr int kRuleEager = 0, kRuleTau = 1, kRuleGuard = 2;
+void set_rescale_rule(int rule);
+int rescale_rule();
 
 }  // namespace fa

@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_backward.restype = i
     lib.fa_testing_set_softmax_spin_limit.argtypes = [i]
     lib.fa_testing_set_softmax_spin_limit.restype = None
+    lib.fa_testing_set_rescale_rule.argtypes = [i]
+    lib.fa_testing_set_rescale_rule.restype = None
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -373,6 +375,16 @@ def testing_set_softmax_spin_limit(limit: int) -> None:
     before its fallback; 0 forces the fallback, a negative value restores the
     default."""
     load_library().fa_testing_set_softmax_spin_limit(int(limit))
+
+
+RESCALE_EAGER, RESCALE_THRESHOLD, RESCALE_GUARD = 0, 1, 2
+
+
+def testing_set_rescale_rule(rule: int) -> None:
+    """Test and ablation hook (include/fa_testing.h): how the bf16 prefill moves
+    its reference max -- RESCALE_GUARD (default), RESCALE_THRESHOLD (tau = 8)
+    or RESCALE_EAGER (every tile)."""
+    load_library().fa_testing_set_rescale_rule(int(rule))
 
 
 def softmax(x, lse_only=False, out=None):

@@ -12,7 +12,9 @@ TFLOP/s with 4*B*H*N*Nk*d FLOPs halved for causal (QK^T and PV only).
 The same run times, each for the same K steps after the same W warm-ups:
 the other prefill workloads (causal d=64, masked high-dynamic-range d=128,
 tiny fp32), the split-KV decode (GB/s), the row softmax (GB/s), the backward
-on two causal shapes and the V1 loop-order ablation.  It times the fp64 CPU oracle on the host's cores over the whole
+on two causal shapes, the V1 loop-order ablation and the rescale-rule
+ablation (the three rules timed in the same run, and how often each rescales,
+replayed on the host).  It times the fp64 CPU oracle on the host's cores over the whole
 headline workload as a reported baseline, and compares every element of the
 timed run's output with it.  Prints one JSON line.
 
@@ -45,7 +47,10 @@ SOFTMAX = "softmax_f32_r1024_c262144"
 BACKWARDS = ("causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 * 1024 * 1024   # plain copy for counter calibration
-SECTIONS = ("headline", "prefill", "decode", "softmax", "backward", "v1")
+SECTIONS = ("headline", "prefill", "decode", "softmax", "backward", "v1", "rescale")
+RESCALE_WORKLOADS = ("causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128")
+GUARD_LOG2 = 32.0      # the guard rule keeps a pair group while its weight sum is below 2^32
+TAU_LOG2 = 8.0         # the threshold rule's growth allowance (log2 units)
 
 # kernel sources each measured path depends on (for the traffic records)
 SOURCES_FWD = ("fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_device.h", "fa_kernels.h", "fa_api.hip")
@@ -139,6 +144,76 @@ def measured_traffic(key):
     if not rec or rec.get("source_hash") != kernel_source_hash(rec.get("sources")):
         return None
     return rec.get("bytes_per_launch")
+
+
+def replay_rescales(q, k, scale, causal, key_len, d, rows_per_wave=32, tile=64, heads=None):
+    """Host replay of the three rescale rules over fp64 scores, in the kernel's
+    grouping (waves of 32 query rows, tiles of 64 keys; the guard checks each
+    pair group -- keys 0..31 and 32..63 of a tile at d=64, the whole tile at
+    d=128 -- before using it).  Per rule: the fraction of (wave, tile) steps
+    on which the wave rescales its accumulators, and per row the mean number
+    of reference moves.  q, k: float64 [BH, N, d] / [BH, Nk, d]; key_len per
+    head (None: all keys)."""
+    import numpy as np
+    BH, N, _ = q.shape
+    Nk = k.shape[1]
+    c = scale / np.log(2.0)
+    groups = [(0, 32), (32, 64)] if d == 64 else [(0, 64)]
+    steps = {"eager": 0, "threshold": 0, "guard": 0}
+    moves = {"eager": 0.0, "threshold": 0.0, "guard": 0.0}
+    total = 0
+    for bh in (heads if heads is not None else range(BH)):
+        kl = Nk if key_len is None else key_len[bh]
+        if kl <= 0:
+            continue
+        s = (q[bh] @ k[bh, :kl].T) * c                      # log2 units
+        j = np.arange(kl)[None, :]
+        if causal:
+            s = np.where(j <= np.arange(N)[:, None] + (Nk - N), s, -np.inf)
+        for w0 in range(0, N, rows_per_wave):
+            sw = s[w0:w0 + rows_per_wave]
+            vis_any = np.isfinite(sw).any(axis=0)
+            ntile = (int(np.nonzero(vis_any)[0].max()) // tile + 1) if vis_any.any() else 0
+            m_eager = np.full(sw.shape[0], -np.inf)
+            m_thr = np.full(sw.shape[0], -np.inf)
+            m_grd = np.full(sw.shape[0], -np.inf)
+            for t in range(ntile):
+                st = sw[:, t * tile:(t + 1) * tile]
+                mx = st.max(axis=1)
+                total += 1
+                if t > 0:
+                    steps["eager"] += 1
+                moves["eager"] += float(np.sum(mx > m_eager))
+                m_eager = np.maximum(m_eager, mx)
+                mv = mx > m_thr + TAU_LOG2
+                if t == 0 or mv.any():
+                    steps["threshold"] += 1 if t > 0 else 0
+                moves["threshold"] += float(np.sum(mv))
+                m_thr = np.where(mv, mx, m_thr)
+                slow = False
+                if t == 0:          # the first tile's max is always taken (prologue)
+                    mvg = mx > m_grd
+                    moves["guard"] += float(np.sum(mvg))
+                    m_grd = np.where(mvg, mx, m_grd)
+                for a, b in groups:
+                    sg = st[:, a:b]
+                    if sg.shape[1] == 0:
+                        continue
+                    ref = np.where(np.isfinite(m_grd), m_grd, 0.0)
+                    with np.errstate(over="ignore", invalid="ignore"):
+                        wsum = np.exp2(sg - ref[:, None]).sum(axis=1)
+                    if not np.isfinite(m_grd).all() or (~(wsum < 2.0 ** GUARD_LOG2)).any():
+                        gm = sg.max(axis=1)
+                        mvg = gm > m_grd
+                        moves["guard"] += float(np.sum(mvg))
+                        m_grd = np.where(mvg, gm, m_grd)
+                        slow = slow or t > 0
+                if slow:
+                    steps["guard"] += 1
+    rows = sum(1 for bh in (heads if heads is not None else range(BH))
+               if (Nk if key_len is None else key_len[bh]) > 0) * N
+    return {r: {"rescaling_steps_frac": round(steps[r] / max(total, 1), 5),
+                "moves_per_row": round(moves[r] / max(rows, 1), 3)} for r in steps} | {"wave_tile_steps": total}
 
 
 def mfma_roofline(flops, per, kernel, traffic_key, alg_bytes, peak=PEAK_BF16_TFLOPS):
@@ -367,6 +442,39 @@ def main():
             "note": "one workgroup per (b, h) as in V1: 64 workgroups on 256 CUs",
         }
         del vi, o1, l1, wv1
+
+    # ----------------------------- rescale rules (FA-4 ablation): timing + host replay
+    if want("rescale"):
+        rules = (("eager", fa.RESCALE_EAGER), ("threshold", fa.RESCALE_THRESHOLD), ("guard", fa.RESCALE_GUARD))
+        ab = {}
+        for name in RESCALE_WORKLOADS:
+            wr = WORKLOADS[name]
+            ri = inp if name == HEADLINE and want("headline") else make_inputs(wr, device=dev)
+            ro = torch.empty_like(ri["q"])
+            rl = torch.empty(wr.B, wr.H, wr.N, device=dev, dtype=torch.float32)
+            kl = ri["key_lens"]
+            rec = {"workload": wr.describe()}
+            try:
+                for rn, code in rules:
+                    fa.testing_set_rescale_rule(code)
+                    ms_r, _ = time_launches(lambda: fa.fa_forward(ri["q"], ri["k"], ri["v"], ro, rl,
+                                                                  causal=wr.causal, key_lens=kl), K, W)
+                    rec[rn + "_ms"] = round(ms_r, 5)
+            finally:
+                fa.testing_set_rescale_rule(fa.RESCALE_GUARD)
+            rec["guard_vs_eager_time"] = round(rec["guard_ms"] / rec["eager_ms"], 4)
+            rec["guard_vs_threshold_time"] = round(rec["guard_ms"] / rec["threshold_ms"], 4)
+            rec["threshold_vs_eager_time"] = round(rec["threshold_ms"] / rec["eager_ms"], 4)
+            # replay: every head of the smaller workloads, 4 heads of the 8192-long one
+            qd = ri["q"].reshape(-1, wr.N, wr.d).double().cpu().numpy()
+            kd = ri["k"].reshape(-1, wr.Nk, wr.d).double().cpu().numpy()
+            klh = None if kl is None else [int(x) for x in kl.tolist() for _ in range(wr.H)]
+            heads = None if wr.B * wr.H * wr.N * wr.Nk <= 2 ** 29 else [0, 9, 18, 31]
+            rec["replay"] = replay_rescales(qd, kd, wr.scale, wr.causal, klh, wr.d, heads=heads)
+            rec["replay"]["heads"] = "all" if heads is None else heads
+            ab[name] = rec
+            del ro, rl, qd, kd
+        out["rescale_ablation"] = ab
 
     # ----------------------------------------------- CPU oracle baseline + parity
     if not args.no_cpu_baseline:

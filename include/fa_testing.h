@@ -20,6 +20,25 @@ extern "C" {
  */
 void fa_testing_set_softmax_spin_limit(int limit);
 
+/*
+ * Rule by which the bf16 prefill (fa_forward with FA_BF16) moves each query
+ * row's reference max and rescales o and l ('Online Softmax -- the
+ * mathematical heart of FlashAttention', section 4; research-hub 'Online
+ * Softmax' page, "Why it matters": FA-4 rescales only when the max shift
+ * threatens stability):
+ *   2 (default)  overflow guard: a tile's weights are taken against the
+ *                current reference and kept unless a weight could reach 2^32;
+ *                only then is the tile's max taken and the reference moved;
+ *   1            threshold: every tile's max is taken, the reference moves
+ *                when it grows by more than 8 (log2 units);
+ *   0            eager: every tile's max is taken and o, l are rescaled on
+ *                every tile (the plain recurrence).
+ * All three give the same result up to rounding.  Any other value restores
+ * the default.  Applies to launches made after the call, process-wide; for
+ * measurement and tests.
+ */
+void fa_testing_set_rescale_rule(int rule);
+
 #ifdef __cplusplus
 }
 #endif

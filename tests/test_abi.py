@@ -48,11 +48,13 @@ def test_testing_header_symbols_are_exported(lib):
     text = open(os.path.join(ROOT, "include", "fa_testing.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*void\s+(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)
-    assert names == ["fa_testing_set_softmax_spin_limit"]
+    assert names == ["fa_testing_set_softmax_spin_limit", "fa_testing_set_rescale_rule"]
     out = subprocess.run(["nm", "-D", "--defined-only", fabuild.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    assert "fa_testing_set_softmax_spin_limit" in out
+    for n in names:
+        assert n in out
     lib.fa_testing_set_softmax_spin_limit(-1)   # host-only: no device work
+    lib.fa_testing_set_rescale_rule(-1)
 
 
 def test_status_strings(lib):

@@ -284,3 +284,45 @@ def test_f32_largest_slice():
     forward_and_check(inp, True, what=f"f32 largest slice causal Nk={Nk}", rows=[0, 1, 17, 36])
     del inp
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ rescale rules
+def _spike_case(B, H, N, Nk, d, seed, first_low):
+    # scores ~ N(0, 1/8) plus single keys whose score jumps by 200 (far past any
+    # weight limit) at positions in the first and the second half of 64-key tiles,
+    # and optionally a first tile 1000 below the rest (the reference must move up
+    # from there); key lengths cut some batches
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, N, d, generator=g)
+    q[..., 0] = 1.0
+    k = 0.25 * torch.randn(B, H, Nk, d, generator=g)
+    k[..., 0] = 0.0
+    for j in (5, 40, 97, 170, 230):
+        if j < Nk:
+            k[:, :, j, 0] = 200.0 * (1 + j % 3)
+    if first_low:
+        k[:, :, :64, 0] = -1000.0
+    v = torch.randn(B, H, Nk, d, generator=g)
+    return {"q": q.to(BF16).to(DEV), "k": k.to(BF16).to(DEV), "v": v.to(BF16).to(DEV),
+            "key_lens": torch.tensor([Nk, 150, 64, 41][:B], dtype=torch.int32, device=DEV)}
+
+
+@pytest.mark.parametrize("rule", [fa.RESCALE_EAGER, fa.RESCALE_THRESHOLD, fa.RESCALE_GUARD])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_rescale_rules(rule, d, causal):
+    # every rule by which the prefill moves its reference max gives the oracle's
+    # result: ordinary scores, a high dynamic range, score spikes in either half
+    # of a tile and a first tile far below the rest (slow paths of the guard rule)
+    fa.testing_set_rescale_rule(rule)
+    try:
+        inp = random_case(2, 3, 200, 333, d, BF16, seed=d + rule, device=DEV, key_lens=[333, 97])
+        forward_and_check(inp, causal, what=f"rule {rule}")
+        inp = random_case(2, 2, 160, 300, d, BF16, seed=3 * d + rule, device=DEV, q_sigma=12.0,
+                          key_lens=[300, 131])
+        forward_and_check(inp, causal, what=f"rule {rule} q~N(0,144)")
+        for first_low in (False, True):
+            inp = _spike_case(4, 2, 130, 260, d, seed=d + 7 * rule, first_low=first_low)
+            forward_and_check(inp, causal, scale=1.0 / 8, what=f"rule {rule} spikes first_low={first_low}")
+    finally:
+        fa.testing_set_rescale_rule(fa.RESCALE_GUARD)
