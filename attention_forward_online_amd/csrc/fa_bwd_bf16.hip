@@ -650,7 +650,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
     const int Npad = (a.N + kTile - 1) / kTile * kTile;
     float *L2 = static_cast<float *>(a.workspace);
     float *Dd = L2 + BH * Npad;
-    const int order = launch_order(a.B, a.H, CAUSAL, a.key_lens);
+    // the dQ kernel streams K and V of its head, the dK/dV kernel Q and dO
+    const int order_q = launch_order(a.B, a.H, CAUSAL, a.key_lens, 2ll * a.Nk * D * 2);
+    const int order_k = launch_order(a.B, a.H, CAUSAL, a.key_lens, 2ll * a.N * D * 2);
     const float c = a.scale * kLog2e;
     if (a.N > 0) {
         // the dQ kernel also writes the D and LSE2 arrays the dK/dV kernel reads
@@ -659,7 +661,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_qt)), dim3(threads), 0, stream,
                                (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                                (const uint16_t *)a.O, (const uint16_t *)a.dO, a.LSE, (uint16_t *)a.dQ,
-                               L2, Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, order, c, a.scale);
+                               L2, Dd, a.key_lens, a.H, a.N, a.Nk, Npad, n_qt, order_q, c, a.scale);
         };
         // at most one query block per CU: two key groups per block
         if (BH * n_qt <= device_cu_count()) dq(bwd_dq_kernel<D, CAUSAL, 2>, 2 * kThreads);
@@ -671,7 +673,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(kern, dim3((unsigned)(BH * n_kt)), dim3(threads), 0, stream,
                                (const uint16_t *)a.Q, (const uint16_t *)a.K, (const uint16_t *)a.V,
                                (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
-                               a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, order, c, a.scale);
+                               a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, order_k, c, a.scale);
         };
         // at most one key block per CU: two query groups per block
         const bool split = BH * n_kt <= device_cu_count();

@@ -125,6 +125,13 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     // phase at d = 64, the S phase at d = 128 (measured: 2-3% each, the other
     // choice neutral)
     constexpr int kPrioPhase = D == 64 ? 2 : 1;
+    // the pairs beside the S MFMAs in a three-stage pipeline (d = 128: two
+    // waves per SIMD at most, so a slot's dependent VALU chain is not hidden by
+    // other waves); d = 64 keeps three waves per SIMD and one pair per slot
+    constexpr bool kStagedPairs = D == 128;
+    // the refill's window loads issued one per S MFMA slot instead of all at
+    // the top of the step
+    constexpr bool kSpreadRefill = false;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
     // the guard checks the pairs made beside the P.V MFMAs before the MFMAs
     // that use them: all of them are made beside the first half
@@ -250,6 +257,15 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     };
     auto dma_k = [&](uint16_t *dst, int t) { dma(IntC<NJK>{}, goffk, K + kv_base, dst, t); };
     auto dma_v = [&](uint16_t *dst, int t) { dma(IntC<NJV>{}, goffv, V + kv_base, dst, t); };
+    // the m-th window load of this wave's share of a tile (for refills spread
+    // over the MFMA slots of a step)
+    auto dma_one = [&](auto nj_c, const uint32_t *goff, const uint16_t *src, uint16_t *dst, int t, int m) {
+        constexpr int NJ = decltype(nj_c)::value;
+        const int j0 = (tbase + t) * kBc;
+        const rsrc_t r = make_rsrc(src + (size_t)j0 * D, (uint32_t)max(kv_end - j0, 0) * D * 2);
+        if (wave + kWaves * m < NJ)
+            buffer_load_lds16(r, (char *)dst + 1024 * (wave + kWaves * m), goff[m]);
+    };
     // Each lane's element offsets within a K and a V stage, computed once: the
     // operands below add only compile-time offsets to them.
     const int k_lane = krow * KS + 8 * g;
@@ -276,6 +292,30 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         const float p1 = exp2_hw(fmaf(s[jb][v + 1], c, -ref));
         rs[q & 3] += p0 + p1;
         pk[ci][e] = pack_bf16x2(p0, p1);
+        pin(rs[q & 3]);
+        pin(pk[ci][e]);
+    };
+    // The same pair in three stages for a software pipeline across MFMA slots
+    // (slot i: arguments of pair i, exponentials of pair i - 1, sum and pack of
+    // pair i - 2), so that no VALU instruction of a slot waits on another of
+    // the same slot: the arithmetic and the rounding are those of p_pair.
+    auto pair_args = [&](const f32x16_t (&s)[2], int q, float (&x)[2]) {
+        const int ci = q >> 2, e = q & 3, jb = ci >> 1, v = 8 * (ci & 1) + 2 * e;
+        x[0] = fmaf(s[jb][v], c, -ref);
+        x[1] = fmaf(s[jb][v + 1], c, -ref);
+        pin(x[0]);
+        pin(x[1]);
+    };
+    auto pair_exp = [&](float (&x)[2]) {
+        x[0] = exp2_hw(x[0]);
+        x[1] = exp2_hw(x[1]);
+        pin(x[0]);
+        pin(x[1]);
+    };
+    auto pair_keep = [&](int q, const float (&p)[2], uint32_t (&pk)[4][4], float (&rs)[4]) {
+        const int ci = q >> 2, e = q & 3;
+        rs[q & 3] += p[0] + p[1];
+        pk[ci][e] = pack_bf16x2(p[0], p[1]);
         pin(rs[q & 3]);
         pin(pk[ci][e]);
     };
@@ -374,10 +414,17 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         dma_k(kst(par), t + 2);
         dma_v(vst(par ^ 1), t + 1);
     };
+    // part m of that refill: K window m, then V window m - MJK
+    auto refill_part = [&](int par, int t, int m) {
+        if (m < MJK)
+            dma_one(IntC<NJK>{}, goffk, K + kv_base, kst(par), t + 2, m);
+        else if (m < MJK + MJV)
+            dma_one(IntC<NJV>{}, goffv, V + kv_base, vst(par ^ 1), t + 1, m - MJK);
+    };
     auto step = [&](auto par_c, auto last_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         constexpr int par = decltype(par_c)::value;
         constexpr bool LAST = decltype(last_c)::value;
-        refill(par, t);
+        if constexpr (!kSpreadRefill) refill(par, t);
         uint32_t pk[4][4];
         // row-sum partials of the pairs being made: those beside the S MFMAs,
         // then (folded into ts first) those beside the P.V MFMAs
@@ -414,14 +461,35 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
             for (int i = 0; i < PD; ++i) kop[i] = k_operand(par ^ 1, i);
         }
         if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(1);
+        if constexpr (kStagedPairs) {
+            // pairs 0 .. NS-1 through the three-stage pipeline, two slots of
+            // drain after the last MFMA
+            float xa[3][2];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            if constexpr (!LAST) {
-                sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
-                if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
+            for (int i = 0; i < NS + 2; ++i) {
+                if constexpr (kSpreadRefill) refill_part(par, t, i);
+                if constexpr (!LAST) {
+                    if (i < NS) {
+                        sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
+                        if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
+                    }
+                }
+                if (i < NS && (!LAST || !half || i < 8)) pair_args(sc, i, xa[i % 3]);
+                if (i >= 1 && i - 1 < NS && (!LAST || !half || i - 1 < 8)) pair_exp(xa[(i - 1) % 3]);
+                if (i >= 2 && (!LAST || !half || i - 2 < 8)) pair_keep(i - 2, xa[(i - 2) % 3], pk, rs);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (!LAST || !half || i < 8) p_pair(sc, i, pk, rs);
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                if constexpr (kSpreadRefill) refill_part(par, t, i);
+                if constexpr (!LAST) {
+                    sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
+                    if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);
+                }
+                if (!LAST || !half || i < 8) p_pair(sc, i, pk, rs);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if constexpr (kPrioPhase == 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (!LAST)
@@ -570,7 +638,7 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
     const long long BH = (long long)a.B * a.H;
     const long long nblocks = BH * n_qtiles;
-    const int order = launch_order(a.B, a.H, CAUSAL, a.key_lens);
+    const int order = launch_order(a.B, a.H, CAUSAL, a.key_lens, 2ll * a.Nk * D * 2);
     // a grid of at most one block per CU leaves each CU with one four-wave
     // workgroup (one wave per SIMD): split every block's keys over two groups
     // of four waves instead.  Such a workgroup needs the LDS of two and runs

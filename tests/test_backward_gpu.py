@@ -3,11 +3,12 @@ fp64 oracle's exact gradients on the same stored inputs.
 
 The GPU path starts from its own forward (bf16 O, fp32 LSE), rounds P and dS to
 bf16 as MFMA operands and accumulates in fp32; dQ, dK, dV are stored in bf16.
-Tolerance per gradient tensor G (bf16): max |G - G_ref| <= 2e-2 * max |G_ref| + 1e-3.
-Derivation: every product carries one bf16 rounding of P or dS (relative
-2^-9) and the output one more (2^-9); the sums over up to a few thousand
-terms of mixed sign keep the relative error near 1e-2 of the tensor's largest
-entry in the worst rows.  fp32 path (fp32 throughout, from the fp32 forward's
+Tolerance per gradient tensor G (bf16): max |G - G_ref| <= 8e-3 * max |G_ref| + 1e-3.
+Derivation: the stored gradient is rounded to bf16 (up to 2^-9 = 0.2% of
+max |G|), and every product in its sum carries one bf16 rounding of P or dS
+(relative 2^-9, of mixed sign over up to a few thousand terms); measured at
+most 0.45% of max |G_ref| over every case here, so 8e-3 (4 x 2^-9) leaves a
+margin of about 1.8.  fp32 path (fp32 throughout, from the fp32 forward's
 O and LSE): max |G - G_ref| <= 2e-5 * max |G_ref| + 1e-6 (fp32 sums over up to
 a few thousand terms; the forward's LSE and O errors of ~1e-6 enter P and D;
 measured below 1e-6 of max |G_ref|).
@@ -27,7 +28,7 @@ from gpu_common import say, to_host
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-TOLS = {torch.bfloat16: (2e-2, 1e-3), torch.float32: (2e-5, 1e-6)}
+TOLS = {torch.bfloat16: (8e-3, 1e-3), torch.float32: (2e-5, 1e-6)}
 
 
 def make(B, H, N, Nk, seed, key_lens=None, d=64, dtype=torch.bfloat16):
@@ -169,6 +170,14 @@ def test_key_length_launch_order(B, H, N, Nk, d):
     kl = [int(x) for x in rng.choice([0, 1, 37, Nk // 2, Nk // 2, Nk, Nk + 9, -3], size=B)]
     q, k, v, do, klt = make(B, H, N, Nk, seed=B + d, key_lens=kl, d=d)
     run_and_check(q, k, v, do, klt, False, what=f"key-length order B={B}")
+
+
+@pytest.mark.parametrize("B,H,N,Nk,d,causal", [(1, 16, 1000, 4500, 128, True), (1, 16, 9000, 300, 64, False)])
+def test_grouped_head_order(B, H, N, Nk, d, causal):
+    # heads whose streamed K/V (dQ kernel) or Q/dO (dK/dV kernel) exceed an XCD's
+    # L2 go in groups of one head: every (head, block) once; three heads in full
+    q, k, v, do, kl = make(B, H, N, Nk, seed=N + Nk, d=d)
+    run_and_check(q, k, v, do, kl, causal, heads=[0, 7, 15], what=f"grouped order N={N} Nk={Nk}")
 
 
 def test_full_size_headline_shape():

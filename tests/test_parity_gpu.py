@@ -326,3 +326,20 @@ def test_bf16_rescale_rules(rule, d, causal):
             forward_and_check(inp, causal, scale=1.0 / 8, what=f"rule {rule} spikes first_low={first_low}")
     finally:
         fa.testing_set_rescale_rule(fa.RESCALE_GUARD)
+
+
+@pytest.mark.parametrize("B,H,N,Nk,d,causal", [(1, 32, 300, 3000, 128, True), (1, 16, 200, 9000, 64, True),
+                                                (2, 16, 130, 4500, 128, False), (1, 8, 64, 16384, 128, True)])
+def test_bf16_grouped_head_order(B, H, N, Nk, d, causal):
+    # when an XCD's heads stream more K/V than its L2 holds, their blocks go in
+    # groups of heads (here groups of 2 and of 1 head): every (head, block) must
+    # be computed exactly once; outputs start as NaN
+    inp = random_case(B, H, N, Nk, d, BF16, seed=N + Nk + d, device=DEV)
+    o = torch.full_like(inp["q"], float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=DEV)
+    say(f"[gpu] fa_forward grouped head order B={B} H={H} N={N} Nk={Nk} d={d} causal={causal}")
+    fa.fa_forward(inp["q"], inp["k"], inp["v"], o, lse, causal=causal)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(to_host(inp["q"]), to_host(inp["k"]), to_host(inp["v"]),
+                                    scale=float(np.float32(1.0 / np.sqrt(d))), causal=causal)
+    compare(o, lse, O_ref, L_ref, BF16, f"grouped head order B={B} H={H} Nk={Nk}")
