@@ -387,36 +387,53 @@ __global__ __launch_bounds__(kThreads) void softmax_reset_kernel(unsigned *ticke
 }
 
 // (m, l) of row r streamed by one workgroup, one 16-byte vector per thread at
-// a time (the bounded wait's fallback; X is never written on this path).
+// a time (the bounded wait's fallback; X is never written on this path),
+// bit for bit the pair the waiting path merges.
 template <typename T>
 __device__ ML stream_row_stats(const Params &p, long long r, ML *sh) {
     constexpr int VN = Elem<T>::kVec;
     constexpr int C = coop_chunk<T>();
-    ML acc{neg_inf(), 0.f};
+    constexpr int NV = coop_nv<T>();
+    const int t = threadIdx.x;
+    // every chunk's pair formed exactly as the workgroup that owns the chunk
+    // forms it (same elements per thread, max first, then the exponentials
+    // summed in the same order, the same workgroup merge), one vector in
+    // registers at a time; thread j keeps the pair of chunk j
+    ML mine{neg_inf(), 0.f};
 #pragma unroll 1
     for (int j = 0; j < p.S; ++j) {
         const ChunkGeom<T, C> g(p, r, j);
-        if (g.load_bytes == 0) continue;
         const rsrc_t rs = make_rsrc(p.X + g.start * (long long)sizeof(T), g.load_bytes);
+        auto vec = [&](int i, float *x) {
+            u32x4_t raw = g.load_bytes == 0
+                ? u32x4_t{0u, 0u, 0u, 0u}
+                : load16<0>(rs, (uint32_t)((i * kThreads + t) * VN * (int)sizeof(T)));
+            if (!g.interior) Elem<T>::mask_raw(raw, (i * kThreads + t) * VN, g.lo, g.hi);
+            Elem<T>::widen(raw, x);
+        };
+        float m = neg_inf();
 #pragma unroll 1
-        for (int i = 0; i < coop_nv<T>(); ++i) {
-            const int k0 = (i * kThreads + (int)threadIdx.x) * VN;
+        for (int i = 0; i < NV; ++i) {
             float x[VN];
-            Elem<T>::widen(load16<0>(rs, (uint32_t)(k0 * (int)sizeof(T))), x);
-            float m = neg_inf();
+            vec(i, x);
 #pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                if (k0 + e < g.lo || k0 + e >= g.hi) x[e] = neg_inf();
-                m = fmaxf(m, x[e]);
-            }
-            const float ms = m == neg_inf() ? 0.f : m;
-            float l = 0.f;
+            for (int e = 0; e < VN; ++e) m = fmaxf(m, x[e]);
+        }
+        const float ms = m == neg_inf() ? 0.f : m;
+        float l = 0.f;
+#pragma unroll 1
+        for (int i = 0; i < NV; ++i) {
+            float x[VN];
+            vec(i, x);
 #pragma unroll
             for (int e = 0; e < VN; ++e) l += exp2_hw((x[e] - ms) * kLog2e);
-            acc = merge(acc, ML{m, l});
         }
+        const ML pair = group_merge<kThreads>(ML{m, l}, sh);
+        __syncthreads();    // sh is written again for the next chunk
+        if (t == j) mine = pair;
     }
-    return group_merge<kThreads>(acc, sh);
+    // then the row's pairs merge exactly as on the path that read them
+    return group_merge<kThreads>(mine, sh);
 }
 
 // Wide rows in one pass over X: a workgroup takes the next (row, chunk)
@@ -428,8 +445,8 @@ __device__ ML stream_row_stats(const Params &p, long long r, ML *sh) {
 // that do not wait on later tickets, so the wait ends whenever the chip holds
 // one row's chunks at once (S <= 128 here, against 1280 resident workgroups
 // at 5 per CU).  The wait is still bounded: past the poll limit the
-// workgroup streams the row itself (same result up to rounding order), so
-// every wave exits.  X must not alias Y on this path (the fallback re-reads X).
+// workgroup streams the row itself (the same pair to the bit), so every
+// wave exits.  X must not alias Y on this path (the fallback re-reads X).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void softmax_coop_kernel(Params p) {
     constexpr int VN = Elem<T>::kVec;

@@ -244,7 +244,8 @@ def test_workspace_reuse_across_calls():
 def test_one_pass_wait_fallback(dtype):
     # forced from the host: with a poll limit of 0 every workgroup of the
     # one-pass kernel computes its row's statistics by streaming the row
-    # itself; the result still matches the oracle
+    # itself; the result still matches the oracle, bit for bit the waiting
+    # path's
     rows, cols = 5, 70001
     x = case(rows, cols, dtype, seed=21)
     say(f"[gpu] fa_softmax one-pass fallback {dtype} rows={rows} cols={cols}")
@@ -256,6 +257,8 @@ def test_one_pass_wait_fallback(dtype):
     check_rows(to_host(x), y, lse, f"fallback {dtype}", dtype)
     y2, lse2 = run(x)
     check_rows(to_host(x), y2, lse2, f"after fallback {dtype}", dtype)
+    # the fallback forms and merges the chunk pairs exactly as the waiting path
+    assert torch.equal(y, y2) and torch.equal(lse, lse2), "fallback differs from the waiting path"
 
 
 # one-pass out-of-place rows hold at most 128 chunks of 64 KiB (16384 fp32 or
