@@ -244,7 +244,9 @@ def mfma_roofline(flops, ms, kernel, traffic_key, alg_bytes, peak=PEAK_BF16_TFLO
     return {"bound": "mfma" if peak == PEAK_BF16_TFLOPS else "alu", "achieved": round(achieved, 2),
             "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(traffic_key), "algorithmic_bytes": alg_bytes,
-            "kernel": kernel, "avg_launch_ms": round(ms, 5)}
+            "kernel": kernel, "ms_per_launch": round(ms, 5),
+            "timing": "HIP events around the timed region / launches (gaps between launches included); "
+                      "the rocprofv3 kernel-trace mean of the same launches is at or below it"}
 
 
 def main():
