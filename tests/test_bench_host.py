@@ -87,3 +87,46 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def _replay_case(tile_values, d=64, n=32):
+    """One wave of n query rows against len(tile_values) 64-key tiles whose
+    scores (log2 units) are tile_values[t] for every key of tile t: q = e_0,
+    k_j = x_j e_0 and scale = ln 2 make the log2-unit score exactly x_j."""
+    import numpy as np
+    nk = 64 * len(tile_values)
+    q = np.zeros((1, n, d))
+    q[0, :, 0] = 1.0
+    k = np.zeros((1, nk, d))
+    for t, x in enumerate(tile_values):
+        k[0, 64 * t:64 * (t + 1), 0] = x
+    return bench.replay_rescales(q, k, float(np.log(2.0)), False, None, d)
+
+
+def test_rescale_replay_counts():
+    # slowly growing tile maxima: the eager rule rescales on every step after
+    # the first and moves the reference each time; the threshold (8) and the
+    # guard (2^32) rules set it on the first tile only
+    r = _replay_case([0.0, 0.5, 1.0, 1.5])
+    assert r["wave_tile_steps"] == 4
+    assert r["eager"] == {"rescaling_steps_frac": 0.75, "moves_per_row": 4.0}
+    assert r["threshold"] == {"rescaling_steps_frac": 0.0, "moves_per_row": 1.0}
+    assert r["guard"] == {"rescaling_steps_frac": 0.0, "moves_per_row": 1.0}
+    # a jump of 20 on the third tile: past the threshold, but 32 weights of
+    # 2^20 stay below the guard's 2^32
+    r = _replay_case([0.0, 0.0, 20.0, 20.0])
+    assert r["eager"]["moves_per_row"] == 2.0
+    assert r["threshold"] == {"rescaling_steps_frac": 0.25, "moves_per_row": 2.0}
+    assert r["guard"] == {"rescaling_steps_frac": 0.0, "moves_per_row": 1.0}
+    # a jump of 40: weights of 2^40 would pass the guard's limit, so it moves
+    # too (once: the later tile is then at its reference)
+    r = _replay_case([0.0, 0.0, 40.0, 40.0])
+    assert r["threshold"] == {"rescaling_steps_frac": 0.25, "moves_per_row": 2.0}
+    assert r["guard"] == {"rescaling_steps_frac": 0.25, "moves_per_row": 2.0}
+    # at d = 64 the guard checks the two 32-key halves of a tile separately:
+    # a jump inside the second half of the first tile is caught there
+    import numpy as np
+    q = np.zeros((1, 32, 64)); q[0, :, 0] = 1.0
+    k = np.zeros((1, 128, 64)); k[0, 32:64, 0] = 40.0; k[0, 64:, 0] = 40.0
+    r = bench.replay_rescales(q, k, float(np.log(2.0)), False, None, 64)
+    assert r["guard"]["moves_per_row"] == 1.0     # the first tile's max (40) is taken up front
