@@ -212,11 +212,11 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[cb][v] = 0.f;
-    // Reference max in log2 units (scale*log2(e)*score).  It moves only when
-    // a tile's max exceeds it by more than kLazyTau (thresholded lazy
-    // rescale, 'Online Softmax' research-hub page, "Why it matters"): the
-    // weights 2^(s - ref) then stay below 2^kLazyTau, and o and l always
-    // share one reference, so o / l and ref + log2 l are exact.
+    // Reference max in log2 units (scale*log2(e)*score), moved by the rescale
+    // rule (RULE): the guard moves it only when a group's weights could reach
+    // kGuardLimit, the threshold rule when a tile's max exceeds it by more
+    // than kLazyTau, the eager rule on every tile.  o and l always share one
+    // reference, so o / l and ref + log2 l are exact under every rule.
     float ms = neg_inf();
     float ref = 0.f;        // the reference the next probabilities use (0 while ms = -inf)
     float l = 0.f;          // this lane's half of the running denominator

@@ -181,7 +181,8 @@ def test_bf16_high_dynamic_range(d, sigma):
 @pytest.mark.parametrize("slope", [0.02, 0.3, -0.3, 3.0])
 def test_bf16_score_ramps(d, slope):
     # scores that rise (or fall) steadily along the keys: the running max moves
-    # by less than, or by much more than, the lazy-rescale threshold per tile;
+    # by less than, or by much more than, a rescale rule tolerates per tile
+    # (threshold 8 in log2 units, guard weights below 2^32);
     # rows of several batches see different key lengths, one of them none
     B, H, N, Nk = 3, 2, 200, 700
     g = torch.Generator().manual_seed(11)
