@@ -180,16 +180,16 @@ def test_grouped_head_order(B, H, N, Nk, d, causal):
     run_and_check(q, k, v, do, kl, causal, heads=[0, 7, 15], what=f"grouped order N={N} Nk={Nk}")
 
 
-def test_full_size_headline_shape():
-    # B4 H16 N=Nk=2048 d64 causal, the forward's headline shape; two heads in full
+def test_full_size_d64_causal_shape():
+    # B4 H16 N=Nk=2048 d64 causal; two heads in full
     w = synth.WORKLOADS["causal_bf16_b4h16_n2048_d64"]
     inp = synth.make_inputs(w, device=DEV)
     do = synth.randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", DEV)
-    run_and_check(inp["q"], inp["k"], inp["v"], do, None, True, heads=[0, 45], what="headline shape")
+    run_and_check(inp["q"], inp["k"], inp["v"], do, None, True, heads=[0, 45], what="d64 causal shape")
 
 
 def test_full_size_long_d128_shape():
-    # B1 H32 N=Nk=8192 d128 causal (the long prefill shape); one head in full
+    # B1 H32 N=Nk=8192 d128 causal (the headline prefill's shape); one head in full
     w = synth.WORKLOADS["causal_bf16_b1h32_n8192_d128"]
     inp = synth.make_inputs(w, device=DEV)
     do = synth.randn_slices((w.B, w.H, w.N, w.d), 1.0, torch.bfloat16, 0, w.name, "do", DEV)

@@ -47,7 +47,9 @@ def test_key_lens_and_scale():
     check(2, 3, 300, 300, 64, True, seed=10, key_lens=[300, 1], scale=0.3)
 
 
-def test_headline_shape_sampled():
+def test_d64_causal_workload_matches_v2():
+    # every output of the V1 loop order against the shipped (V2) kernel at the
+    # B4 H16 N=Nk=2048 d64 causal workload
     w = synth.WORKLOADS["causal_bf16_b4h16_n2048_d64"]
     inp = synth.make_inputs(w, device=DEV)
     say(f"[gpu] fa_forward_v1 full size {w.describe()}")
