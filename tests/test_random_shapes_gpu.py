@@ -4,7 +4,7 @@ Query and key lengths from 1 to 700 (so workgroups hold partial query blocks,
 waves with no rows, and odd and even tile counts), causal or not, with or
 without per-batch key lengths (including 0 and values past Nk).  Same
 tolerances as the fixed-shape tests (bf16 forward 2e-2 on O, 1e-3 on LSE; fp32
-1e-5 on both; backward 2e-2 of the largest gradient entry + 1e-3), and rows or
+1e-5 on both; backward 8e-3 of the largest gradient entry + 1e-3), and rows or
 keys that see nothing must be exactly zero."""
 from __future__ import annotations
 
