@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_softmax.hip", "fa_bwd_bf16.hip", "fa_bwd_f32.hip", "fa_fwd_v1.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_softmax.hip", "fa_bwd_bf16.hip", "fa_bwd_f32.hip", "fa_fwd_v1.hip", "fa_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -9,6 +9,7 @@
 
 #include "fa.h"
 #include "fa_kernels.h"
+#include "fa_probe.h"
 #include "fa_testing.h"
 
 namespace {
@@ -270,5 +271,17 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
 void fa_testing_set_softmax_spin_limit(int limit) { fa::set_softmax_spin_limit(limit); }
 
 void fa_testing_set_rescale_rule(int rule) { fa::set_rescale_rule(rule); }
+
+fa_status fa_probe_mfma(float *sink, int blocks, int iters, void *stream) {
+    if (!sink || !aligned4(sink) || blocks < 1 || blocks > kMaxGridX || iters < 1) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_probe_mfma(sink, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_probe_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream) {
+    if ((bytes > 0 && (!src || !aligned16(src))) || bytes % 16 != 0 || !sink || !aligned4(sink) ||
+        blocks < 1 || blocks > kMaxGridX)
+        return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_probe_read(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

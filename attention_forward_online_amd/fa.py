@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_testing_set_softmax_spin_limit.restype = None
     lib.fa_testing_set_rescale_rule.argtypes = [i]
     lib.fa_testing_set_rescale_rule.restype = None
+    lib.fa_probe_mfma.argtypes = [vp, i, i, vp]
+    lib.fa_probe_mfma.restype = i
+    lib.fa_probe_read.argtypes = [vp, sz, vp, i, vp]
+    lib.fa_probe_read.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -385,6 +389,48 @@ def testing_set_rescale_rule(rule: int) -> None:
     its reference max -- RESCALE_GUARD (default), RESCALE_THRESHOLD (tau = 8)
     or RESCALE_EAGER (every tile)."""
     load_library().fa_testing_set_rescale_rule(int(rule))
+
+
+PROBE_THREADS = 256                  # threads per probe workgroup (include/fa_probe.h)
+PROBE_MFMA_FLOPS = 4 * 8 * 32768     # bf16 FLOPs per probe-MFMA workgroup and iteration
+
+
+def probe_mfma(blocks: int, iters: int, sink: Optional[torch.Tensor] = None, device=None, stream=None):
+    """Measurement probe (include/fa_probe.h): `blocks` workgroups stream
+    `iters` rounds of eight bf16 MFMAs (four chains) per wave.  Executed FLOPs =
+    blocks * iters * PROBE_MFMA_FLOPS.  Returns the fp32 sink (one sum per
+    thread)."""
+    lib = _lib or load_library()
+    if sink is None:
+        sink = torch.empty(blocks * PROBE_THREADS, dtype=torch.float32,
+                           device=device if device is not None else "cuda")
+    _check_dev("sink", sink, torch.float32)
+    if sink.numel() < blocks * PROBE_THREADS:
+        raise ValueError("sink holds fewer than 256 * blocks values")
+    idx = sink.get_device()
+    st = _launch(idx, stream, lambda h: lib.fa_probe_mfma(_ptr(sink), int(blocks), int(iters), h))
+    if st != FA_OK:
+        raise FaError(st, "fa_probe_mfma", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+    return sink
+
+
+def probe_read(src: torch.Tensor, blocks: int = 2048, sink: Optional[torch.Tensor] = None, stream=None):
+    """Measurement probe (include/fa_probe.h): read all bytes of `src` once with
+    16-byte loads from `blocks` workgroups.  Returns the int32 sink whose XOR
+    over all entries is the XOR of the buffer's 32-bit words."""
+    lib = _lib or load_library()
+    _check_dev("src", src)
+    idx = src.get_device()
+    if sink is None:
+        sink = torch.empty(blocks * PROBE_THREADS, dtype=torch.int32, device=src.device)
+    _check_dev("sink", sink, torch.int32, idx)
+    if sink.numel() < blocks * PROBE_THREADS:
+        raise ValueError("sink holds fewer than 256 * blocks values")
+    nbytes = src.numel() * src.element_size()
+    st = _launch(idx, stream, lambda h: lib.fa_probe_read(_ptr(src), nbytes, _ptr(sink), int(blocks), h))
+    if st != FA_OK:
+        raise FaError(st, "fa_probe_read", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+    return sink
 
 
 def softmax(x, lse_only=False, out=None):

@@ -33,6 +33,14 @@ run first times the headline cold (reported as `cold_start`, the same W and K),
 then the split-KV decode (its own record; 2.5 ms of HBM-bound work per call),
 and then times the headline again with the same W and K: that second
 measurement is `value`, the sustained rate a continuously loaded GPU delivers.
+
+Measured ceilings (`ceilings`): right after the decode, a bare streaming read
+of the decode's K tensor, and right after the headline, a bare stream of bf16
+MFMAs with operands in registers (the probes of include/fa_probe.h), each with
+the same W and K.  The published peaks assume a 2.4 GHz clock the chip does not
+hold under sustained matrix-core load; each roofline record also gives its
+rate as a fraction of the measured ceiling of its bound
+(`frac_of_measured_ceiling`).
 """
 from __future__ import annotations
 
@@ -59,6 +67,9 @@ SOFTMAX = "softmax_f32_r1024_c262144"
 BACKWARDS = ("causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 * 1024 * 1024   # plain copy for counter calibration
+PROBE_MFMA_BLOCKS = 512          # 2048 waves: two per SIMD, as the d=128 prefill runs
+PROBE_MFMA_ITERS = 2000          # about half a millisecond per call
+PROBE_READ_BLOCKS = 2048
 SECTIONS = ("headline", "prefill", "decode", "softmax", "backward", "v1", "rescale")
 RESCALE_WORKLOADS = ("causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128")
 GUARD_LOG2 = 32.0      # the guard rule keeps a pair group while its weight sum is below 2^32
@@ -303,6 +314,7 @@ def main():
         del src, dst
 
     out = {"metric": METRIC}
+    ceilings = {}
     # ---------------------------------------------------------------- headline
     w = WORKLOADS[HEADLINE]
     if want("headline") or want("backward") or not args.no_cpu_baseline:
@@ -340,6 +352,20 @@ def main():
                          "traffic": measured_traffic("decode/" + DECODE),
                          "kernels": "decode_split_kernel + decode_combine_kernel"},
         }
+        # measured ceiling of the decode: a bare streaming read of its K tensor
+        # (the same 16-byte nontemporal loads, no arithmetic, include/fa_probe.h)
+        sink_r = torch.empty(PROBE_READ_BLOCKS * fa.PROBE_THREADS, dtype=torch.int32, device=dev)
+        ms_r = time_launches(lambda: fa.probe_read(di["k"], PROBE_READ_BLOCKS, sink_r), K, W)
+        rbytes = di["k"].numel() * di["k"].element_size()
+        read_gbs = rbytes / (ms_r * 1e-3) / 1e9
+        ceilings["hbm_read_stream"] = {
+            "gbs": round(read_gbs, 1), "frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+            "ms_per_call": round(ms_r, 4), "bytes_per_call": rbytes,
+            "probe": f"fa_probe_read: {PROBE_READ_BLOCKS} workgroups of 256 threads reading 64 KiB chunks "
+                     "in 16-byte nontemporal loads, the decode workload's K tensor, timed right after "
+                     "the decode"}
+        out["decode"]["roofline"]["frac_of_measured_ceiling"] = round(gbs / read_gbs, 4)
+        del sink_r
 
     if want("headline"):
         # one fa_forward call launches exactly one kernel, fwd_bf16_kernel<128, causal>
@@ -365,6 +391,21 @@ def main():
             "roofline": mfma_roofline(flops, ms_step, "fwd_bf16_kernel<128,true,1,2>",
                                       "forward/" + HEADLINE, prefill_bytes(w)),
         })
+        # measured ceiling of the prefill: a bare stream of bf16 MFMAs (operands in
+        # registers, no softmax, no memory traffic, include/fa_probe.h), timed
+        # right after the headline with the same clock state, W and K
+        sink_m = torch.empty(PROBE_MFMA_BLOCKS * fa.PROBE_THREADS, dtype=torch.float32, device=dev)
+        ms_m = time_launches(lambda: fa.probe_mfma(PROBE_MFMA_BLOCKS, PROBE_MFMA_ITERS, sink_m), K, W)
+        mfl = PROBE_MFMA_BLOCKS * PROBE_MFMA_ITERS * fa.PROBE_MFMA_FLOPS
+        mfma_tflops = mfl / (ms_m * 1e-3) / 1e12
+        ceilings["mfma_bf16_stream"] = {
+            "tflops": round(mfma_tflops, 2), "frac_of_peak": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+            "ms_per_call": round(ms_m, 4), "flops_per_call": mfl,
+            "probe": f"fa_probe_mfma: {PROBE_MFMA_BLOCKS} workgroups of 4 waves (2 per SIMD), "
+                     f"{PROBE_MFMA_ITERS} rounds of 8 v_mfma_f32_32x32x16_bf16 (4 chains) per wave on random bf16 "
+                     "operands held in registers"}
+        out["roofline"]["frac_of_measured_ceiling"] = round(value / mfma_tflops, 4)
+        del sink_m
     if want("decode"):
         del di, od, ld, ws
         torch.cuda.empty_cache()
@@ -390,6 +431,9 @@ def main():
                "tflops": round(fl / (ms_o * 1e-3) / 1e12, 2),
                "flops_per_call": fl,
                "roofline": mfma_roofline(fl, ms_o, kname, "forward/" + name, prefill_bytes(wo, kll), peak)}
+        if "mfma_bf16_stream" in ceilings and wo.dtype != "f32":
+            rec["roofline"]["frac_of_measured_ceiling"] = round(
+                rec["roofline"]["achieved"] / ceilings["mfma_bf16_stream"]["tflops"], 4)
         if kll is not None:
             rec["key_lens"] = kll
             rec["flops_convention"] = "effective: 4*H*N*d*sum(key_lens) (visible keys only)"
@@ -535,6 +579,8 @@ def main():
                          "nan": bool(np.isnan(og).any() or np.isnan(lg).any()),
                          "tolerance": {"O": 2e-2, "LSE": 1e-3}}
         del O_ref, L_ref, og, lg
+    if ceilings:
+        out["ceilings"] = ceilings
     print(json.dumps(out), flush=True)
 
 

@@ -242,3 +242,27 @@ def test_backward_workspace_and_arguments(lib):
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         fa.load_library(str(tmp_path / "libfa.so"))
+
+
+def test_probe_header_symbols_are_exported_and_check_arguments(lib):
+    # include/fa_probe.h: the measurement probes; every call here fails the
+    # host-side checks, so nothing is launched
+    text = open(os.path.join(ROOT, "include", "fa_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*fa_status\s+(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    assert names == ["fa_probe_mfma", "fa_probe_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", fabuild.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert n in out
+    bad = fa.FA_ERR_INVALID_ARG
+    assert lib.fa_probe_mfma(None, 1, 1, None) == bad
+    assert lib.fa_probe_mfma(P, 0, 1, None) == bad
+    assert lib.fa_probe_mfma(P, 1, 0, None) == bad
+    assert lib.fa_probe_mfma(P + 2, 1, 1, None) == bad
+    assert lib.fa_probe_read(None, 16, P, 1, None) == bad
+    assert lib.fa_probe_read(None, 0, None, 1, None) == bad
+    assert lib.fa_probe_read(P, 16, None, 1, None) == bad
+    assert lib.fa_probe_read(P, 17, P, 1, None) == bad
+    assert lib.fa_probe_read(P + 8, 16, P, 1, None) == bad
+    assert lib.fa_probe_read(P, 16, P, 0, None) == bad
