@@ -129,9 +129,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     // waves per SIMD at most, so a slot's dependent VALU chain is not hidden by
     // other waves); d = 64 keeps three waves per SIMD and one pair per slot
     constexpr bool kStagedPairs = D == 128;
-    // the refill's window loads issued one per S MFMA slot instead of all at
-    // the top of the step
-    constexpr bool kSpreadRefill = false;
     static_assert(PAIRS2 % 2 == 0 && PAIRS2 / 2 + 4 <= NP2, "P.V section too short");
     // the guard checks the pairs made beside the P.V MFMAs before the MFMAs
     // that use them: all of them are made beside the first half
@@ -257,15 +254,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
     };
     auto dma_k = [&](uint16_t *dst, int t) { dma(IntC<NJK>{}, goffk, K + kv_base, dst, t); };
     auto dma_v = [&](uint16_t *dst, int t) { dma(IntC<NJV>{}, goffv, V + kv_base, dst, t); };
-    // the m-th window load of this wave's share of a tile (for refills spread
-    // over the MFMA slots of a step)
-    auto dma_one = [&](auto nj_c, const uint32_t *goff, const uint16_t *src, uint16_t *dst, int t, int m) {
-        constexpr int NJ = decltype(nj_c)::value;
-        const int j0 = (tbase + t) * kBc;
-        const rsrc_t r = make_rsrc(src + (size_t)j0 * D, (uint32_t)max(kv_end - j0, 0) * D * 2);
-        if (wave + kWaves * m < NJ)
-            buffer_load_lds16(r, (char *)dst + 1024 * (wave + kWaves * m), goff[m]);
-    };
     // Each lane's element offsets within a K and a V stage, computed once: the
     // operands below add only compile-time offsets to them.
     const int k_lane = krow * KS + 8 * g;
@@ -414,17 +402,10 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         dma_k(kst(par), t + 2);
         dma_v(vst(par ^ 1), t + 1);
     };
-    // part m of that refill: K window m, then V window m - MJK
-    auto refill_part = [&](int par, int t, int m) {
-        if (m < MJK)
-            dma_one(IntC<NJK>{}, goffk, K + kv_base, kst(par), t + 2, m);
-        else if (m < MJK + MJV)
-            dma_one(IntC<NJV>{}, goffv, V + kv_base, vst(par ^ 1), t + 1, m - MJK);
-    };
     auto step = [&](auto par_c, auto last_c, int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         constexpr int par = decltype(par_c)::value;
         constexpr bool LAST = decltype(last_c)::value;
-        if constexpr (!kSpreadRefill) refill(par, t);
+        refill(par, t);
         uint32_t pk[4][4];
         // row-sum partials of the pairs being made: those beside the S MFMAs,
         // then (folded into ts first) those beside the P.V MFMAs
@@ -467,7 +448,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
             float xa[3][2];
 #pragma unroll
             for (int i = 0; i < NS + 2; ++i) {
-                if constexpr (kSpreadRefill) refill_part(par, t, i);
                 if constexpr (!LAST) {
                     if (i < NS) {
                         sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
@@ -482,7 +462,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : (D == 64 ? 3 : 
         } else {
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
-                if constexpr (kSpreadRefill) refill_part(par, t, i);
                 if constexpr (!LAST) {
                     sn[i & 1] = mfma32(kop[i % PD], qf[i >> 1], i < 2 ? f32x16_t{} : sn[i & 1]);
                     if (i + PD < NS) kop[i % PD] = k_operand(par ^ 1, i + PD);

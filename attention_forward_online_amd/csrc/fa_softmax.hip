@@ -188,7 +188,8 @@ struct ChunkGeom {
         const long long mat_end16 = (p.total_bytes + 15) & ~15LL;
         long long avail = (row_end16 < mat_end16 ? row_end16 : mat_end16) - start * (long long)sizeof(T);
         if (hi <= lo) avail = 0;
-        load_bytes = (uint32_t)(avail < 0 ? 0 : (avail > (long long)C * sizeof(T) ? (long long)C * sizeof(T) : avail));
+        const long long cap = (long long)(C * sizeof(T));
+        load_bytes = (uint32_t)(avail < 0 ? 0 : (avail > cap ? cap : avail));
     }
 };
 
