@@ -22,7 +22,9 @@
 //                     order makes P and dS the B operand of dV^T += dO^T P and
 //                     dK^T += Q^T dS directly, dO^T and Q^T come from transpose
 //                     reads, and each lane ends with 16-byte pieces of its key's
-//                     dK and dV rows.
+//                     dK and dV rows.  At d = 128 (bwd_dkdv_paired_kernel) two
+//                     waves share each 32 keys: one makes S, P and dV and hands
+//                     P to the other, which makes dP, dS and dK.
 // Masking follows the forward exactly: causal key j <= i + (Nk - N), keys at
 // or past key_lens[b] invisible; invisible pairs get P = 0, hence dS = 0.
 // Both streaming kernels load their tiles from HBM straight into LDS (buffer
@@ -331,14 +333,12 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_
     }
 }
 
-// dK, dV: 4 waves x 32 keys; Q/dO tiles of 64 queries through two LDS stages.
-// MODE 0 computes both; at d = 128 both accumulators do not fit next to the
-// operands, so MODE 1 (dV only: S, P, dV) and MODE 2 (dK only: S, dP, dS, dK)
-// run as two launches.  KSPLIT = 2 (grids of at most one key block per CU):
-// two groups of four waves share the block, group g taking the g-th half of
-// its query tiles with its own stages; the partial sums are added through LDS.
-enum { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
-template <int D, bool CAUSAL, int MODE, int KSPLIT>
+// dK, dV at d = 64 (d = 128: bwd_dkdv_paired_kernel below): 4 waves x 32 keys;
+// Q/dO tiles of 64 queries through two LDS stages.  KSPLIT = 2 (grids of at
+// most one key block per CU): two groups of four waves share the block, group
+// g taking the g-th half of its query tiles with its own stages; the partial
+// sums are added through LDS.
+template <int D, bool CAUSAL, int KSPLIT>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
     constexpr int TILE = kTile * kRowElems<D>;
     constexpr int KK = D / 16;
     constexpr int CB = D / 32;
-    constexpr bool WANT_DV = MODE != kOnlyDK, WANT_DK = MODE != kOnlyDV;
+    static_assert(D == 64, "both accumulators beside the operands fit at d = 64 only");
 
     // one array per stage (see the dQ kernel); LD holds the tile's 64 LSE2
     // values followed by its 64 D values
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         kf[kk] = buffer_load16(ksrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
-        if constexpr (WANT_DK) vf[kk] = buffer_load16(vsrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
+        vf[kk] = buffer_load16(vsrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
     }
     wait_vmem_all();
 
@@ -518,45 +518,37 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
                 }
                 return x;
             };
-            // P (and dS) of queries 2e, 2e + 1 of block qb as bf16 pairs
+            // P and dS of queries 2e, 2e + 1 of block qb as bf16 pairs
             auto p_pair = [&](int qb, int e) {
                 const int v = 2 * e;
                 const float l0 = lv[e >> 1][v & 3], l1 = lv[e >> 1][(v & 3) + 1];
                 const float p0 = exp2_hw(fmaf(s[qb][v], c, -l0));
                 const float p1 = exp2_hw(fmaf(s[qb][v + 1], c, -l1));
-                if constexpr (WANT_DV) {
-                    pp[qb][e] = pack_bf16x2(p0, p1);
-                    pin(pp[qb][e]);
-                }
-                if constexpr (WANT_DK) {
-                    pd[qb][e] = pack_bf16x2(p0 * dp[qb][v], p1 * dp[qb][v + 1]);   // dP - D
-                    pin(pd[qb][e]);
-                }
+                pp[qb][e] = pack_bf16x2(p0, p1);
+                pin(pp[qb][e]);
+                pd[qb][e] = pack_bf16x2(p0 * dp[qb][v], p1 * dp[qb][v + 1]);   // dP - D
+                pin(pd[qb][e]);
             };
             auto grad_mfma = [&](int cb, int qb, int h) {
-                if constexpr (WANT_DV)
-                    adv[cb] = mfma32(t_operand(Gc, cb, qb, h),
-                                     u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2], pp[qb][4 * h + 3]},
-                                     adv[cb]);
-                if constexpr (WANT_DK)
-                    adk[cb] = mfma32(t_operand(Qc, cb, qb, h),
-                                     u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2], pd[qb][4 * h + 3]},
-                                     adk[cb]);
+                adv[cb] = mfma32(t_operand(Gc, cb, qb, h),
+                                 u32x4_t{pp[qb][4 * h], pp[qb][4 * h + 1], pp[qb][4 * h + 2], pp[qb][4 * h + 3]},
+                                 adv[cb]);
+                adk[cb] = mfma32(t_operand(Qc, cb, qb, h),
+                                 u32x4_t{pd[qb][4 * h], pd[qb][4 * h + 1], pd[qb][4 * h + 2], pd[qb][4 * h + 3]},
+                                 adk[cb]);
             };
             rows_block(Qc, kf, 0, s[0]);
-            if constexpr (WANT_DK) {
-                dp[0] = minus_d(0);
+            dp[0] = minus_d(0);
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) dp[0] = mfma32(row_operand(Gc, 0, kk), vf[kk], dp[0]);
-            }
+            for (int kk = 0; kk < KK; ++kk) dp[0] = mfma32(row_operand(Gc, 0, kk), vf[kk], dp[0]);
             if (need_mask) mask_block(0);
             load_l(0);
-            if constexpr (WANT_DK) dp[1] = minus_d(1);
-            // S (and dP) MFMAs of block 1, two P pairs of block 0 per S step
+            dp[1] = minus_d(1);
+            // S and dP MFMAs of block 1, two P pairs of block 0 per S step
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 s[1] = mfma32(row_operand(Qc, 1, kk), kf[kk], kk == 0 ? f32x16_t{} : s[1]);
-                if constexpr (WANT_DK) dp[1] = mfma32(row_operand(Gc, 1, kk), vf[kk], dp[1]);
+                dp[1] = mfma32(row_operand(Gc, 1, kk), vf[kk], dp[1]);
 #pragma unroll
                 for (int e = 8 * kk / KK; e < 8 * (kk + 1) / KK; ++e) p_pair(0, e);
                 __builtin_amdgcn_sched_barrier(0);
@@ -593,8 +585,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
         // group 1 hands its partial sums to group 0 through the Q and dO stages
         // (every wave is past its last LDS read, no load in flight): one
         // 256-byte row per accumulator register, lane-indexed
-        constexpr int NA = (WANT_DK ? 1 : 0) + (WANT_DV ? 1 : 0);
-        constexpr int RW = 16 * CB * NA;
+        constexpr int RW = 2 * 16 * CB;
         constexpr int R0 = (int)(sizeof(Qs0) / 256);
         static_assert(kWaves * RW <= 4 * R0, "partial sums do not fit the stages");
         auto mrow = [&](int k) -> float * {
@@ -603,14 +594,14 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
             return (float *)base + 64 * rr + lane;
         };
         // dK partials in rows 0 .. 16 CB - 1 of the wave's range, dV after them
-        constexpr int VOFF = WANT_DK ? 16 * CB : 0;
+        constexpr int VOFF = 16 * CB;
         if (grp == 1) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    if constexpr (WANT_DK) *mrow(16 * cb + v) = adk[cb][v];
-                    if constexpr (WANT_DV) *mrow(VOFF + 16 * cb + v) = adv[cb][v];
+                    *mrow(16 * cb + v) = adk[cb][v];
+                    *mrow(VOFF + 16 * cb + v) = adv[cb][v];
                 }
         }
         __syncthreads();
@@ -619,8 +610,8 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                if constexpr (WANT_DK) adk[cb][v] += *mrow(16 * cb + v);
-                if constexpr (WANT_DV) adv[cb][v] += *mrow(VOFF + 16 * cb + v);
+                adk[cb][v] += *mrow(16 * cb + v);
+                adv[cb][v] += *mrow(VOFF + 16 * cb + v);
             }
     }
 
@@ -638,8 +629,319 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
                     wk[e] = pack_bf16x2(adk[cb][8 * h + 2 * e] * scale, adk[cb][8 * h + 2 * e + 1] * scale);
                     wv[e] = pack_bf16x2(adv[cb][8 * h + 2 * e], adv[cb][8 * h + 2 * e + 1]);
                 }
-                if constexpr (WANT_DK) *(u32x4_t *)(krow_out + 32 * cb + 16 * h + 8 * g) = wk;
-                if constexpr (WANT_DV) *(u32x4_t *)(vrow_out + 32 * cb + 16 * h + 8 * g) = wv;
+                *(u32x4_t *)(krow_out + 32 * cb + 16 * h + 8 * g) = wk;
+                *(u32x4_t *)(vrow_out + 32 * cb + 16 * h + 8 * g) = wv;
+            }
+    }
+}
+
+// dK and dV of 128 keys in one pass (d = 128, where one wave cannot hold
+// both accumulators beside its operands): 8 waves, waves w and w + 4 take the
+// same 32 keys 32w .. 32w + 31 of the workgroup's 128 and share a SIMD.  Wave
+// w (P side) keeps the K fragment: S = Q K^T, P = 2^(s c - LSE2) and
+// dV^T += dO^T P; it hands its fp32 P to wave w + 4 through LDS.  Wave w + 4
+// (dS side) keeps the V fragment and runs one Q/dO tile behind:
+// dP - D = dO V^T - D, dS = P (dP - D) and dK^T += Q^T dS.  Iteration t: the
+// P side works on tile t, the dS side on tile t - 1, tile t + 1 loads (three
+// Q/dO stages).  Before the iteration's first barrier the P side makes S and
+// P of tile t in registers while the dS side reads P(t - 1) and makes dP and
+// dS; after it the P side writes P(t) into the one P buffer and adds dV while
+// the dS side adds dK; the second barrier publishes P(t) and the loaded tile.
+// Each tile's S and P are made once and its Q/dO cross HBM once (two
+// launches, one per gradient, make S twice), and every P, dS and gradient
+// comes from the same operations in the same order as in those two launches.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, const float *__restrict__ L2, const float *__restrict__ Dd,
+    const int32_t *__restrict__ key_lens, int H, int N, int Nk, int Npad, int n_ktiles,
+    int order, float c, float scale) {
+    constexpr int TILE = kTile * kRowElems<D>;
+    constexpr int KK = D / 16;
+    constexpr int CB = D / 32;
+    constexpr int NW = 2 * kWaves;
+
+    // three stages, one array each (see the dQ kernel)
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE], Qs1[TILE], Qs2[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Gs0[TILE], Gs1[TILE], Gs2[TILE];   // dO
+    __shared__ __attribute__((aligned(16))) float LD0[2 * kTile], LD1[2 * kTile], LD2[2 * kTile];
+    // P of one tile, [key group][32-query block][register pair][lane][2]: each
+    // pair of a group is one 512-byte row, written and read as 8 bytes per lane
+    __shared__ __attribute__((aligned(1024))) float Ps[kWaves * 2 * 8 * 64 * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave_id >= 0 && wave_id < NW);
+    const int side = wave_id >> 2;              // 0: S, P, dV; 1: dP, dS, dK
+    const int wave = wave_id & (kWaves - 1);    // its 32 keys
+    const int li = lane & 31, g = lane >> 5;
+    const int qperm = perm32(li);
+    const int trow = (li & 15) >> 2;
+    const int tcol = perm32(4 * ((li & 3) + 4 * (li >> 4)));
+    auto qst = [&](int st) -> uint16_t * { return st == 0 ? Qs0 : st == 1 ? Qs1 : Qs2; };
+    auto gst = [&](int st) -> uint16_t * { return st == 0 ? Gs0 : st == 1 ? Gs1 : Gs2; };
+    auto ldst = [&](int st) -> float * { return st == 0 ? LD0 : st == 1 ? LD1 : LD2; };
+
+    int bh, rank;
+    block_in_order(blockIdx.x, gridDim.x / n_ktiles, n_ktiles, order, H, key_lens, Nk, bh, rank);
+    const int b = bh / H;
+    const int off = Nk - N;
+    const int kv_lim = visible_len(key_lens, b, Nk);
+    const size_t q_base = (size_t)bh * N * D;
+    const size_t kv_base = (size_t)bh * Nk * D;
+
+    const int k0 = rank * kBk;
+    const int wk0 = k0 + wave * 32;
+    const int key = wk0 + li;
+    const bool key_vis = key < kv_lim;
+    const int i_first = CAUSAL ? max(0, k0 - off) : 0;
+    const int t_first = k0 < kv_lim ? i_first / kTile : 0;
+    const int n_q = (N + kTile - 1) / kTile;
+    const int ntiles = (k0 < kv_lim && i_first < N) ? n_q - t_first : 0;
+
+    const rsrc_t lsrc = make_rsrc(L2 + (size_t)bh * Npad, (uint32_t)Npad * 4);
+    const rsrc_t dsrc = make_rsrc(Dd + (size_t)bh * Npad, (uint32_t)Npad * 4);
+    // the side's fragment of its keys: K (P side) or V (dS side)
+    const rsrc_t fsrc = make_rsrc((side == 0 ? K : V) + kv_base, (uint32_t)Nk * D * 2);
+    u32x4_t fr[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) fr[kk] = buffer_load16(fsrc, (uint32_t)(key * D + 16 * kk + 8 * g) * 2);
+    f32x16_t ag[CB];   // dV (P side) or dK (dS side)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ag[cb][v] = 0.f;
+
+    // Q/dO tiles straight into LDS, the 1 KiB windows spread over all 8 waves:
+    // load j of a wave is Q window j / 2 (j even) or dO window j / 2 (j odd),
+    // load 2 MJ the tile's 64 LSE2 (wave 0) or D (wave 1) values
+    constexpr int RB = kRowElems<D> * 2;
+    constexpr int NJ = kTile * RB / 1024, MJ = (NJ + NW - 1) / NW, NL = 2 * MJ + 1;
+    static_assert(NJ * 1024 == kTile * RB, "stage is not a whole number of windows");
+    static_assert(NL <= 2 * KK, "loads outnumber the MFMA slots they are spread over");
+    uint32_t goff[MJ];
+#pragma unroll
+    for (int m = 0; m < MJ; ++m) {
+        const int p = 1024 * (wave_id + NW * m) + 16 * lane;
+        const int r = p / RB, q = (p % RB) / 16;
+        goff[m] = (q < D / 8 && r < kTile) ? (uint32_t)(r * D * 2 + 16 * q) : 0x7ffffff0u;
+    }
+    // the Q and dO ranges of tile t (whole tiles of the padded LSE2/D arrays)
+    auto tile_src = [&](int t, rsrc_t &qr, rsrc_t &gr) {
+        const int i0 = (t_first + t) * kTile;
+        const uint32_t bytes = (uint32_t)max(N - i0, 0) * D * 2;
+        qr = make_rsrc(Q + q_base + (size_t)i0 * D, bytes);
+        gr = make_rsrc(dO + q_base + (size_t)i0 * D, bytes);
+    };
+    auto load_one = [&](int j, int t, int st, const rsrc_t &qr, const rsrc_t &gr) {
+        const int i0 = (t_first + t) * kTile;
+        if (j < 2 * MJ) {
+            const int m = j >> 1;
+            if (wave_id + NW * m < NJ)
+                buffer_load_lds16(j & 1 ? gr : qr, (char *)(j & 1 ? gst(st) : qst(st)) + 1024 * (wave_id + NW * m),
+                                  goff[m]);
+        } else if (wave_id < 2 && lane < 16) {
+            buffer_load_lds16(wave_id == 0 ? lsrc : dsrc, (char *)ldst(st) + 256 * wave_id,
+                              (uint32_t)(i0 + 4 * lane) * 4);
+        }
+    };
+    auto active = [&](int t) {
+        const int i_last = (t_first + t) * kTile + kTile - 1;
+        return wk0 < kv_lim && (!CAUSAL || i_last + off >= wk0);
+    };
+    // Each lane's element offsets within a tile for the row and transpose
+    // reads, and its float offset within Ps.  Every iteration takes fresh copies
+    // (an empty asm redefines them), so the stage addresses derived from them
+    // are formed in the iteration rather than held in registers across the loop.
+    const int row_lane0 = lds_at<D>(qperm, 8 * g);
+    const int tr_lane0 = lds_at<D>(8 * g + trow, tcol);
+    const int pw_lane0 = wave * (2 * 8 * 128) + 2 * lane;
+    int row_lane = row_lane0, tr_lane = tr_lane0, pw_lane = pw_lane0;
+    auto row_operand = [&](const uint16_t *R, int qb, int kk) {
+        return *(const u32x4_t *)&R[row_lane + lds_at<D>(32 * qb, 16 * kk)];
+    };
+    auto t_operand = [&](const uint16_t *T, int cb, int qb, int h) {
+        const auto *tb = (const __attribute__((address_space(3))) uint16_t *)T + tr_lane;
+        const int r0 = 32 * qb + 16 * h;
+        const u32x2_t lo = lds_read_tr16(tb + lds_at<D>(r0, 32 * cb));
+        const u32x2_t hi = lds_read_tr16(tb + lds_at<D>(r0 + 4, 32 * cb));
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // n MFMAs, MFMA i taking the LDS operand op(i) read two MFMAs ahead, with
+    // body(i, operand) issuing it and any other work beside it
+    auto pipelined = [&](auto n_c, auto op, auto body) {
+        constexpr int n = decltype(n_c)::value;
+        u32x4_t ring[2];
+        ring[0] = op(0);
+        ring[1] = op(1);
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            const u32x4_t cur = ring[i & 1];
+            if (i + 2 < n) ring[i & 1] = op(i + 2);
+            body(i, cur);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // gradient MFMA i adds half h = (i / CB) % 2 of block i / (2 CB) to
+    // accumulator i % CB: consecutive MFMAs are independent, and each
+    // accumulator adds its four terms in block, half order
+    auto grad_mfmas = [&](const uint16_t *T, const uint32_t (&pk)[2][8], auto extra) {
+        pipelined(IntC<4 * CB>{}, [&](int i) { return t_operand(T, i % CB, i / (2 * CB), (i / CB) & 1); },
+                  [&](int i, const u32x4_t &a) {
+                      const int qb = i / (2 * CB), cb = i % CB, h = (i / CB) & 1;
+                      ag[cb] = mfma32(a, u32x4_t{pk[qb][4 * h], pk[qb][4 * h + 1], pk[qb][4 * h + 2], pk[qb][4 * h + 3]},
+                                      ag[cb]);
+                      extra(i);
+                  });
+    };
+
+    // iteration t, stage of tile t: ST (compile time)
+    auto iteration = [&](auto st_c, int t) {
+        constexpr int ST = decltype(st_c)::value, ST_PREV = (ST + 2) % 3, ST_NEXT = (ST + 1) % 3;
+        pw_lane = pw_lane0;
+        asm volatile("" : "+v"(pw_lane));
+        float *const pw = Ps + pw_lane;   // this key group's P rows
+        const bool load_next = t + 1 < ntiles;
+        rsrc_t qr, gr;
+        tile_src(t + 1, qr, gr);
+        auto issue = [&](int j) {
+            if (load_next && j < NL) load_one(j, t + 1, ST_NEXT, qr, gr);
+        };
+        // S, then P (P side); dP - D, then dS (dS side); block qb in
+        // x[qb], register v holding query i0 + 32qb + 16(v/8) + 8g + v%8
+        f32x16_t x[2];
+        uint32_t pk[2][8];
+        const bool act0 = side == 0 && t < ntiles && active(t);
+        const bool act1 = side == 1 && t >= 1 && active(t - 1);
+        if (act0) {
+            const int i0 = (t_first + t) * kTile;
+            const uint16_t *Qc = qst(ST);
+            const float *LDc = ldst(ST);
+            pipelined(IntC<2 * KK>{}, [&](int i) { return row_operand(Qc, i & 1, i >> 1); },
+                      [&](int i, const u32x4_t &a) {
+                          const int qb = i & 1, kk = i >> 1;
+                          x[qb] = mfma32(a, fr[kk], kk == 0 ? f32x16_t{} : x[qb]);
+                          issue(i);
+                      });
+            if (!key_vis || (i0 + kTile > N) || (CAUSAL && i0 + off < wk0 + 31)) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int i = i0 + 32 * qb + 16 * (v >> 3) + 8 * g + (v & 7);
+                        if (!key_vis || i >= N || (CAUSAL && key > i + off)) x[qb][v] = neg_inf();
+                    }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x4_t lv[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i8 = 32 * qb + 16 * h + 8 * g;
+                    lv[2 * h] = *(const f32x4_t *)&LDc[i8];
+                    lv[2 * h + 1] = *(const f32x4_t *)&LDc[i8 + 4];
+                }
+                // P of queries 2e, 2e + 1: fp32 in place of S, bf16 pair for dV
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = 2 * e;
+                    const float p0 = exp2_hw(fmaf(x[qb][v], c, -lv[e >> 1][v & 3]));
+                    const float p1 = exp2_hw(fmaf(x[qb][v + 1], c, -lv[e >> 1][(v & 3) + 1]));
+                    x[qb][v] = p0;
+                    x[qb][v + 1] = p1;
+                    pk[qb][e] = pack_bf16x2(p0, p1);
+                    pin(pk[qb][e]);
+                }
+            }
+        } else if (act1) {
+            const float *LDc = ldst(ST_PREV);
+            const uint16_t *Gc = gst(ST_PREV);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i8 = 32 * qb + 16 * h + 8 * g;
+                    const f32x4_t a = *(const f32x4_t *)&LDc[kTile + i8];
+                    const f32x4_t bb = *(const f32x4_t *)&LDc[kTile + i8 + 4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[qb][8 * h + e] = a[e];
+                        x[qb][8 * h + 4 + e] = bb[e];
+                    }
+                }
+            pipelined(IntC<2 * KK>{}, [&](int i) { return row_operand(Gc, i & 1, i >> 1); },
+                      [&](int i, const u32x4_t &a) {
+                          x[i & 1] = mfma32(a, fr[i >> 1], x[i & 1]);
+                          issue(i);
+                      });
+            // dS from P(t - 1), written by the P side before the last barrier
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x2_t pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = *(const f32x2_t *)&pw[(8 * qb + e) * 128];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = 2 * e;
+                    pk[qb][e] = pack_bf16x2(pv[e][0] * x[qb][v], pv[e][1] * x[qb][v + 1]);
+                    pin(pk[qb][e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) issue(j);
+        }
+        // P(t - 1) has been read: the P side may overwrite the buffer
+        __syncthreads();
+        if (act0) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) *(f32x2_t *)&pw[(8 * qb + e) * 128] = f32x2_t{x[qb][2 * e], x[qb][2 * e + 1]};
+            grad_mfmas(gst(ST), pk, [](int) {});
+        } else if (act1) {
+            grad_mfmas(qst(ST_PREV), pk, [](int) {});
+        }
+        wait_vmem_all();
+        __syncthreads();
+    };
+    if (ntiles > 0) {
+        rsrc_t qr, gr;
+        tile_src(0, qr, gr);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) load_one(j, 0, 0, qr, gr);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    const int nit = ntiles > 0 ? ntiles + 1 : 0;
+    int t = 0;
+    for (; t + 3 <= nit; t += 3) {
+        iteration(IntC<0>{}, t);
+        iteration(IntC<1>{}, t + 1);
+        iteration(IntC<2>{}, t + 2);
+    }
+    if (t < nit) iteration(IntC<0>{}, t);
+    if (t + 1 < nit) iteration(IntC<1>{}, t + 1);
+
+    // accumulator register 8h + e of block cb holds d = 32cb + 16h + 8g + e of this lane's key
+    if (key < Nk) {
+        uint16_t *orow = (side == 0 ? dV : dK) + kv_base + (size_t)key * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4_t w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float a0 = ag[cb][8 * h + 2 * e], a1 = ag[cb][8 * h + 2 * e + 1];
+                    if (side == 1) {
+                        a0 *= scale;
+                        a1 *= scale;
+                    }
+                    w[e] = pack_bf16x2(a0, a1);
+                }
+                *(u32x4_t *)(orow + 32 * cb + 16 * h + 8 * g) = w;
             }
     }
 }
@@ -675,17 +977,14 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream) {
                                (const uint16_t *)a.dO, (uint16_t *)a.dK, (uint16_t *)a.dV, L2, Dd,
                                a.key_lens, a.H, a.N, a.Nk, Npad, n_kt, order_k, c, a.scale);
         };
-        // at most one key block per CU: two query groups per block
-        const bool split = BH * n_kt <= device_cu_count();
         if constexpr (D == 64) {
-            if (split) dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth, 2>, 2 * kThreads);
-            else dkdv(bwd_dkdv_kernel<D, CAUSAL, kBoth, 1>, kThreads);
-        } else if (split) {
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV, 2>, 2 * kThreads);
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK, 2>, 2 * kThreads);
+            // at most one key block per CU: two query groups per block
+            if (BH * n_kt <= device_cu_count()) dkdv(bwd_dkdv_kernel<D, CAUSAL, 2>, 2 * kThreads);
+            else dkdv(bwd_dkdv_kernel<D, CAUSAL, 1>, kThreads);
         } else {
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDV, 1>, kThreads);
-            dkdv(bwd_dkdv_kernel<D, CAUSAL, kOnlyDK, 1>, kThreads);
+            // 8-wave workgroups at any grid size: measured faster than the two
+            // query groups of the d = 64 kernel on grids of one block per CU
+            dkdv(bwd_dkdv_paired_kernel<D, CAUSAL>, 2 * kThreads);
         }
     }
     return hipGetLastError();

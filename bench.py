@@ -492,7 +492,7 @@ def main():
                 "ms_per_call": round(ms_b, 5), "tflops": round(bflops / (ms_b * 1e-3) / 1e12, 2),
                 "flops_per_call": bflops,
                 "flops_convention": "5 GEMMs (QK^T, dP, dV, dK, dQ) = 2.5 x forward, halved for causal",
-                "roofline": mfma_roofline(bflops, ms_b, "bwd_dq_kernel + bwd_dkdv_kernel",
+                "roofline": mfma_roofline(bflops, ms_b, "bwd_dq_kernel + " + ("bwd_dkdv_kernel" if wb.d == 64 else "bwd_dkdv_paired_kernel"),
                                           "backward/" + name, alg),
             }
             del dob, dq, dk, dv, wsb

@@ -5,7 +5,8 @@ No kernel may use scratch memory (per-lane stack: register spills or private
 arrays the compiler could not keep in registers), and the kernels whose
 occupancy the measured rates rest on must keep it: the bf16 prefill at d = 64
 and the bf16 backward's dQ kernel at three waves per SIMD (at most 168 VGPRs of
-the 512 a SIMD lane holds), the bf16 prefill at d = 128 and the dK/dV kernel at
+the 512 a SIMD lane holds), the bf16 prefill at d = 128, the d = 64 dK/dV
+kernel and the d = 128 paired dK/dV kernel (one 8-wave workgroup per CU) at
 two."""
 from __future__ import annotations
 
@@ -71,7 +72,8 @@ OCCUPANCY = [
     ("fa_fwd_bf16.hip", r"fwd_bf16_kernelILi128ELb[01]ELi1E", 2),
     ("fa_bwd_bf16.hip", r"bwd_dq_kernelILi64ELb[01]ELi1E", 3),
     ("fa_bwd_bf16.hip", r"bwd_dq_kernelILi128ELb[01]ELi1E", 2),
-    ("fa_bwd_bf16.hip", r"bwd_dkdv_kernelILi(64|128)ELb[01]ELi[012]ELi1E", 2),
+    ("fa_bwd_bf16.hip", r"bwd_dkdv_kernelILi64ELb[01]ELi1E", 2),
+    ("fa_bwd_bf16.hip", r"bwd_dkdv_paired_kernelILi128ELb[01]E", 2),
 ]
 
 
