@@ -10,7 +10,7 @@ from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_SCRATC
                  fa_backward_workspace_bytes, fa_decode_splitkv, fa_decode_workspace_bytes,
                  fa_forward, fa_softmax, fa_softmax_workspace_bytes, load_library, softmax,
                  status_str, testing_set_softmax_spin_limit, testing_set_rescale_rule,
-                 RESCALE_EAGER, RESCALE_THRESHOLD, RESCALE_GUARD, probe_mfma, probe_read,
+                 RESCALE_EAGER, RESCALE_THRESHOLD, RESCALE_GUARD, probe_mfma, probe_read, probe_copy,
                  PROBE_MFMA_FLOPS, PROBE_THREADS)
 
 __all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_SCRATCH_LIMIT",
@@ -21,4 +21,4 @@ __all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_SCR
            "fa_decode_workspace_bytes", "fa_forward", "fa_softmax", "fa_softmax_workspace_bytes",
            "load_library", "softmax", "status_str", "testing_set_softmax_spin_limit",
            "testing_set_rescale_rule", "RESCALE_EAGER", "RESCALE_THRESHOLD", "RESCALE_GUARD",
-           "probe_mfma", "probe_read", "PROBE_MFMA_FLOPS", "PROBE_THREADS"]
+           "probe_mfma", "probe_read", "probe_copy", "PROBE_MFMA_FLOPS", "PROBE_THREADS"]

@@ -284,4 +284,13 @@ fa_status fa_probe_read(const void *src, size_t bytes, uint32_t *sink, int block
     return from_hip(fa::launch_probe_read(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream) {
+    if (bytes % 16 != 0 || blocks < 1 || blocks > kMaxGridX) return FA_ERR_INVALID_ARG;
+    if (bytes == 0) return FA_OK;
+    if (!src || !dst || !aligned16(src) || !aligned16(dst)) return FA_ERR_INVALID_ARG;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    if (s < d + bytes && d < s + bytes) return FA_ERR_INVALID_ARG;   // overlapping ranges
+    return from_hip(fa::launch_probe_copy(src, dst, bytes, blocks, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

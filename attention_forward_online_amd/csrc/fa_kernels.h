@@ -83,8 +83,10 @@ constexpr int kRuleEager = 0, kRuleTau = 1, kRuleGuard = 2;
 void set_rescale_rule(int rule);
 int rescale_rule();
 
-// measurement probes (fa_probe.hip): a bf16 MFMA stream and a streaming read
+// measurement probes (fa_probe.hip): a bf16 MFMA stream, a streaming read and
+// a streaming copy
 hipError_t launch_probe_mfma(float *sink, int blocks, int iters, hipStream_t stream);
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, int blocks, hipStream_t stream);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream);
 
 }  // namespace fa

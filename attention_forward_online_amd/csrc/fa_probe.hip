@@ -1,6 +1,6 @@
-// fa_probe.hip -- two measurement kernels that compute nothing of the attention
+// fa_probe.hip -- measurement kernels that compute nothing of the attention
 // path: the sustained rate of the matrix cores on a stream of independent bf16
-// MFMAs, and the sustained HBM read bandwidth of 16-byte loads.  Benchmarks
+// MFMAs, and the sustained HBM bandwidth of 16-byte loads (and stores).  Benchmarks
 // put the attention kernels' rates next to what this GPU delivers for the bare
 // operation each of them is bound by (the published peaks assume a clock the
 // chip does not hold under sustained matrix-core load).
@@ -85,6 +85,28 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
     sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = x;
 }
 
+// Streaming copy: the read probe's chunking, each vector stored to the same
+// offset of dst with a nontemporal store after all kReadUnroll loads of its
+// chunk are in flight.
+__global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const u32x4_t *__restrict__ src,
+                                                                   u32x4_t *__restrict__ dst, size_t n16) {
+    constexpr size_t kChunk = (size_t)kProbeThreads * kReadUnroll;
+    const size_t nch = n16 / kChunk;
+    const size_t per = (nch + gridDim.x - 1) / gridDim.x;   // chunks per workgroup
+    const size_t c0 = (size_t)blockIdx.x * per, c1 = c0 + per < nch ? c0 + per : nch;
+    for (size_t ch = c0; ch < c1; ++ch) {
+        const size_t i0 = ch * kChunk + threadIdx.x;
+        u32x4_t v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i0 + (size_t)u * kProbeThreads);
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i0 + (size_t)u * kProbeThreads);
+    }
+    for (size_t i = nch * kChunk + (size_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * kProbeThreads)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
 
 hipError_t launch_probe_mfma(float *sink, int blocks, int iters, hipStream_t stream) {
@@ -95,6 +117,12 @@ hipError_t launch_probe_mfma(float *sink, int blocks, int iters, hipStream_t str
 hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *sink, int blocks, hipStream_t stream) {
     hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
                        static_cast<const u32x4_t *>(src), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, int blocks, hipStream_t stream) {
+    hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
+                       static_cast<const u32x4_t *>(src), static_cast<u32x4_t *>(dst), bytes / 16);
     return hipGetLastError();
 }
 

@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_probe_mfma.restype = i
     lib.fa_probe_read.argtypes = [vp, sz, vp, i, vp]
     lib.fa_probe_read.restype = i
+    lib.fa_probe_copy.argtypes = [vp, vp, sz, i, vp]
+    lib.fa_probe_copy.restype = i
     lib.fa_status_str.argtypes = [i]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -431,6 +433,23 @@ def probe_read(src: torch.Tensor, blocks: int = 2048, sink: Optional[torch.Tenso
     if st != FA_OK:
         raise FaError(st, "fa_probe_read", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
     return sink
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, blocks: int = 2048, stream=None) -> torch.Tensor:
+    """Measurement probe (include/fa_probe.h): copy all bytes of `src` into
+    `dst` (same device, same byte size, no overlap) with 16-byte loads and
+    stores from `blocks` workgroups.  Returns dst."""
+    lib = _lib or load_library()
+    _check_dev("src", src)
+    idx = src.get_device()
+    _check_dev("dst", dst, None, idx)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst must hold as many bytes as src")
+    st = _launch(idx, stream, lambda h: lib.fa_probe_copy(_ptr(src), _ptr(dst), nbytes, int(blocks), h))
+    if st != FA_OK:
+        raise FaError(st, "fa_probe_copy", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+    return dst
 
 
 def softmax(x, lse_only=False, out=None):

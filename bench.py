@@ -35,9 +35,10 @@ and then times the headline again with the same W and K: that second
 measurement is `value`, the sustained rate a continuously loaded GPU delivers.
 
 Measured ceilings (`ceilings`): right after the decode, a bare streaming read
-of the decode's K tensor, and right after the headline, a bare stream of bf16
-MFMAs with operands in registers (the probes of include/fa_probe.h), each with
-the same W and K.  The published peaks assume a 2.4 GHz clock the chip does not
+of the decode's K tensor; right after the headline, a bare stream of bf16
+MFMAs with operands in registers; right after the row softmax, a bare
+streaming copy of its input into its output (the probes of
+include/fa_probe.h), each with the same W and K.  The published peaks assume a 2.4 GHz clock the chip does not
 hold under sustained matrix-core load; each roofline record also gives its
 rate as a fraction of the measured ceiling of its bound
 (`frac_of_measured_ceiling`).
@@ -70,6 +71,7 @@ COPY_BYTES = 512 * 1024 * 1024   # plain copy for counter calibration
 PROBE_MFMA_BLOCKS = 512          # 2048 waves: two per SIMD, as the d=128 prefill runs
 PROBE_MFMA_ITERS = 2000          # about half a millisecond per call
 PROBE_READ_BLOCKS = 2048
+PROBE_COPY_BLOCKS = 4096         # fastest of 512 .. 16384 in a sweep over a 1 GiB copy
 SECTIONS = ("headline", "prefill", "decode", "softmax", "backward", "v1", "rescale")
 RESCALE_WORKLOADS = ("causal_bf16_b4h16_n2048_d64", "causal_bf16_b1h32_n8192_d128", "masked_bf16_b2h8_n4096_d128")
 GUARD_LOG2 = 32.0      # the guard rule keeps a pair group while its weight sum is below 2^32
@@ -462,6 +464,19 @@ def main():
                          "traffic": measured_traffic("softmax/" + SOFTMAX),
                          "kernels": "softmax_reset_kernel + softmax_coop_kernel (one pass over X)"},
         }
+        # measured ceiling of the softmax: a bare streaming copy of X into Y (the
+        # same bytes read and written, 16-byte nontemporal loads and stores,
+        # include/fa_probe.h)
+        ms_c = time_launches(lambda: fa.probe_copy(xs, ys, PROBE_COPY_BLOCKS), K, W)
+        cbytes = 2 * xs.numel() * xs.element_size()
+        copy_gbs = cbytes / (ms_c * 1e-3) / 1e9
+        ceilings["hbm_copy_stream"] = {
+            "gbs": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "ms_per_call": round(ms_c, 4), "bytes_per_call": cbytes,
+            "probe": f"fa_probe_copy: {PROBE_COPY_BLOCKS} workgroups of 256 threads copying 64 KiB chunks "
+                     "in 16-byte nontemporal loads and stores, the softmax workload's X into its Y "
+                     "(bytes read plus bytes written), timed right after the softmax"}
+        out["softmax"]["roofline"]["frac_of_measured_ceiling"] = round(gbs / copy_gbs, 4)
         del xs, ys, ls, wss
         torch.cuda.empty_cache()
 

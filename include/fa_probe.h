@@ -1,11 +1,12 @@
 /*
  * fa_probe.h -- measurement probes of libfa.so.  Not part of the
- * computational ABI in fa.h: two kernels that measure, on the GPU at hand, the
+ * computational ABI in fa.h: kernels that measure, on the GPU at hand, the
  * rate of the bare operation each attention kernel is bound by -- a stream of
  * bf16 matrix-core products for the prefill, a streaming HBM read for the
- * split-KV decode -- so that a benchmark can report its kernels against these
- * measured ceilings beside the published peaks.  Both run asynchronously on
- * `stream` (a hipStream_t, NULL for the default stream) and allocate nothing.
+ * split-KV decode, a streaming copy for the row softmax -- so that a
+ * benchmark can report its kernels against these measured ceilings beside the
+ * published peaks.  All run asynchronously on `stream` (a hipStream_t, NULL
+ * for the default stream) and allocate nothing.
  */
 #ifndef FA_PROBE_H
 #define FA_PROBE_H
@@ -47,6 +48,19 @@ fa_status fa_probe_mfma(float *sink, int blocks, int iters, void *stream);
  * fails.
  */
 fa_status fa_probe_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream);
+
+/*
+ * Streaming copy: `blocks` workgroups of 256 threads copy the `bytes` bytes at
+ * src to dst (both device, 16-byte aligned, the two ranges disjoint, bytes a
+ * multiple of 16) once, in 16-byte nontemporal loads and stores, each
+ * workgroup one contiguous run of 64 KiB chunks as in the streaming read: the
+ * traffic of a kernel that reads an array once and writes one of the same
+ * size.  bytes = 0 does nothing (src and dst may then be NULL).
+ * Errors: FA_ERR_INVALID_ARG for blocks < 1, bytes not a multiple of 16, or
+ * (bytes > 0) a NULL or misaligned src or dst, or ranges that overlap;
+ * FA_ERR_HIP if the launch fails.
+ */
+fa_status fa_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream);
 
 #ifdef __cplusplus
 }

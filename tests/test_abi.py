@@ -250,7 +250,7 @@ def test_probe_header_symbols_are_exported_and_check_arguments(lib):
     text = open(os.path.join(ROOT, "include", "fa_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*fa_status\s+(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)
-    assert names == ["fa_probe_mfma", "fa_probe_read"]
+    assert names == ["fa_probe_mfma", "fa_probe_read", "fa_probe_copy"]
     out = subprocess.run(["nm", "-D", "--defined-only", fabuild.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     for n in names:
@@ -266,3 +266,13 @@ def test_probe_header_symbols_are_exported_and_check_arguments(lib):
     assert lib.fa_probe_read(P, 17, P, 1, None) == bad
     assert lib.fa_probe_read(P + 8, 16, P, 1, None) == bad
     assert lib.fa_probe_read(P, 16, P, 0, None) == bad
+    Q = P + (1 << 20)
+    assert lib.fa_probe_copy(P, Q, 16, 0, None) == bad          # no workgroup
+    assert lib.fa_probe_copy(P, Q, 24, 1, None) == bad          # not a multiple of 16
+    assert lib.fa_probe_copy(None, Q, 16, 1, None) == bad
+    assert lib.fa_probe_copy(P, None, 16, 1, None) == bad
+    assert lib.fa_probe_copy(P + 8, Q, 16, 1, None) == bad      # misaligned
+    assert lib.fa_probe_copy(P, Q + 8, 16, 1, None) == bad
+    assert lib.fa_probe_copy(P, P + 16, 32, 1, None) == bad     # overlapping ranges
+    assert lib.fa_probe_copy(P + 16, P, 32, 1, None) == bad
+    assert lib.fa_probe_copy(None, None, 0, 1, None) == fa.FA_OK   # nothing to copy, nothing launched

@@ -1,7 +1,8 @@
 """GPU checks of the measurement probes of include/fa_probe.h: the streaming
-read touches every byte exactly once (its XOR checksum equals the host's), and
-the matrix-core stream really executes its products (its sums are finite,
-nonzero and grow linearly with the iteration count)."""
+read touches every byte exactly once (its XOR checksum equals the host's), the
+streaming copy reproduces its source byte for byte and writes nothing past its
+end, and the matrix-core stream really executes its products (its sums are
+finite, nonzero and grow linearly with the iteration count)."""
 from __future__ import annotations
 
 import numpy as np
@@ -38,6 +39,20 @@ def test_probe_read_checksum(nbytes, blocks):
     torch.cuda.synchronize()
     got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
     assert got == host_xor(buf)
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (16 * 1000 + 16 * 7, 5), (64 << 20, 2048),
+                                           ((64 << 20) + 48, 7), (1 << 20, 3000)])
+def test_probe_copy_reproduces_source(nbytes, blocks):
+    g = torch.Generator(device="cpu").manual_seed(nbytes % 7919)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g).to(DEV)
+    big = torch.full((nbytes // 4 + 64,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    dst = big[: nbytes // 4]
+    say(f"[gpu] fa_probe_copy bytes={nbytes} blocks={blocks}")
+    fa.probe_copy(src, dst, blocks=blocks)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert bool((big[nbytes // 4:] == 0x5A5A5A5A).all())
 
 
 def test_probe_mfma_executes_every_product():
