@@ -124,22 +124,26 @@ def test_scale_and_ragged_batch_heads():
     run_and_check(q, k, v, do, kl, True, scale=0.3, what="scale 0.3 causal")
 
 
-def test_empty_sides():
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_sides(d):
     # no queries: dK = dV = 0; no keys: dQ = 0
-    q, k, v, do, kl = make(1, 2, 0, 70, seed=3)
+    q, k, v, do, kl = make(1, 2, 0, 70, seed=3, d=d)
     o, lse = fa.attention(q, k, v)
     dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do)
     torch.cuda.synchronize()
     assert dq.shape == q.shape and torch.all(dk == 0) and torch.all(dv == 0)
-    q, k, v, do, kl = make(1, 2, 50, 0, seed=4)
+    q, k, v, do, kl = make(1, 2, 50, 0, seed=4, d=d)
     o, lse = fa.attention(q, k, v)
     dq, dk, dv = fa.attention_backward(q, k, v, o, lse, do)
     torch.cuda.synchronize()
     assert torch.all(dq == 0) and dk.shape == k.shape
 
 
-def test_deterministic():
-    q, k, v, do, kl = make(2, 4, 300, 300, seed=5)
+@pytest.mark.parametrize("d", [64, 128])
+def test_deterministic(d):
+    # no atomics anywhere: two calls give the same bits (at d = 128 with P handed
+    # between the two waves of each key group through LDS)
+    q, k, v, do, kl = make(2, 4, 300, 300, seed=5, d=d)
     o, lse = fa.attention(q, k, v, causal=True)
     a = fa.attention_backward(q, k, v, o, lse, do, causal=True)
     b = fa.attention_backward(q, k, v, o, lse, do, causal=True)
@@ -153,10 +157,11 @@ def test_deterministic():
 @pytest.mark.parametrize("d", [64, 128])
 def test_split_grid_boundary(d, causal, extra_heads):
     # a grid of at most one block per CU runs each block's tiles in two halves whose
-    # partial sums are added at the end: the key tiles of a 128-query dQ block, the
-    # query tiles of a 128-key dK/dV block (N = 300 and Nk = 330 give three blocks per
-    # head in both kernels); one more head per batch puts the same inputs on the
-    # unsplit path.  Key lengths: one tile (split 1 / 0), two tiles, an odd count, all;
+    # partial sums are added at the end: the key tiles of a 128-query dQ block, and
+    # at d = 64 the query tiles of a 128-key dK/dV block (N = 300 and Nk = 330 give
+    # three blocks per head in both kernels; the d = 128 dK/dV kernel runs its
+    # 8-wave workgroups at any grid size); one more head per batch puts the same
+    # inputs on the unsplit path.  Key lengths: one tile (split 1 / 0), two tiles, an odd count, all;
     # causal with Nk > N puts the diagonal in the second half.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     B, N, Nk = 4, 300, 330
