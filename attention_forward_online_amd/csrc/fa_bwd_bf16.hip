@@ -755,10 +755,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
     // of the last (an empty asm redefines it), so the P addresses are formed in
     // the iteration rather than held in registers across the loop (held, they
     // pushed the kernel past 256 VGPRs).
-    const int row_lane = lds_at<D>(qperm, 8 * g);
-    const int tr_lane = lds_at<D>(8 * g + trow, tcol);
+    const int row_lane0 = lds_at<D>(qperm, 8 * g);
+    const int tr_lane0 = lds_at<D>(8 * g + trow, tcol);
     const int pw_lane0 = wave * (2 * 8 * 128) + 2 * lane;
-    int pw_lane = pw_lane0;
+    int row_lane = row_lane0, tr_lane = tr_lane0, pw_lane = pw_lane0;
     auto row_operand = [&](const uint16_t *R, int qb, int kk) {
         return *(const u32x4_t *)&R[row_lane + lds_at<D>(32 * qb, 16 * kk)];
     };
