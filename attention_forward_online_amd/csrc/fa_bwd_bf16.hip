@@ -264,21 +264,24 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dq_
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (need_mask) mask_block(1);
+            // dQ MFMA i of a block adds half h = i / CB to accumulator i % CB:
+            // consecutive MFMAs are independent, each accumulator adds its
+            // halves in order
             constexpr int NQ = 2 * CB;
             __builtin_amdgcn_s_setprio(1);
             u32x4_t kt = kt_operand(cur, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < NQ; ++i) {
                 const u32x4_t a = kt;
-                if (i + 1 < NQ) kt = kt_operand(cur, (i + 1) >> 1, 0, (i + 1) & 1);
-                dq_mfma(i >> 1, 0, i & 1, a);
+                if (i + 1 < NQ) kt = kt_operand(cur, (i + 1) % CB, 0, (i + 1) / CB);
+                dq_mfma(i % CB, 0, i / CB, a);
 #pragma unroll
                 for (int e = 8 * i / NQ; e < 8 * (i + 1) / NQ; ++e) ds_pair(1, e);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) dq_mfma(i >> 1, 1, i & 1, kt_operand(cur, i >> 1, 1, i & 1));
+            for (int i = 0; i < NQ; ++i) dq_mfma(i % CB, 1, i / CB, kt_operand(cur, i % CB, 1, i / CB));
         }
         wait_vmem_all();
         __syncthreads();
@@ -559,14 +562,14 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < 2 * CB; ++i) {
-                grad_mfma(i >> 1, 0, i & 1);
+                grad_mfma(i % CB, 0, i / CB);
 #pragma unroll
                 for (int e = 8 * i / (2 * CB); e < 8 * (i + 1) / (2 * CB); ++e) p_pair(1, e);
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-            for (int i = 0; i < 2 * CB; ++i) grad_mfma(i >> 1, 1, i & 1);
+            for (int i = 0; i < 2 * CB; ++i) grad_mfma(i % CB, 1, i / CB);
         }
         wait_vmem_all();
         __syncthreads();
