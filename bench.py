@@ -276,7 +276,7 @@ def main():
                          "counters scale the kernels' counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(every workload here is measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
     only = None

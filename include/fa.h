@@ -44,7 +44,7 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, negative size, bad flag, too-small workspace */
-    FA_ERR_UNSUPPORTED = 2,   /* valid request this build has no kernel for (e.g. bf16 with d = 96) */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request the library has no kernel for (e.g. bf16 with d = 96) */
     FA_ERR_HIP = 3,           /* the HIP runtime reported an error at launch */
     FA_ERR_SCRATCH_LIMIT = 4  /* the request needs more than the library's fixed scratch
                                  (fa_decode_splitkv_noalloc only) */
