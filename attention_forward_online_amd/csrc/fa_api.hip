@@ -244,7 +244,7 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if (dtype == FA_F32 && d > 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_F32 && d > 256) return FA_ERR_UNSUPPORTED;
     if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0 || (N == 0 && Nk == 0)) return FA_OK;
     if ((long long)B * H * (long long)(N > Nk ? N : Nk) * d > kMaxElems) return FA_ERR_INVALID_ARG;
@@ -261,7 +261,8 @@ fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O
     const size_t need = fa::backward_workspace_bytes(B, H, N);
     if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
         return FA_ERR_INVALID_ARG;
-    const long long blocks = (long long)B * H * (((N > Nk ? N : Nk) + 63) / 64);
+    // the smallest workgroups hold 16 rows (fp32, d > 128)
+    const long long blocks = (long long)B * H * (((N > Nk ? N : Nk) + 15) / 16);
     if (blocks > kMaxGridX) return FA_ERR_INVALID_ARG;
     fa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, key_lens, B, H, N, Nk, d, scale, causal, workspace};
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -226,8 +226,9 @@ size_t fa_backward_workspace_bytes(int B, int H, int N);
  *   (B, H, N) bytes; contents on entry do not matter.  Calls sharing a
  *   workspace must not overlap in time.
  *   Supported: FA_BF16 with d in {64, 128} (bf16 MFMA operands, fp32
- *   accumulation) and FA_F32 with 1 <= d <= 128 (fp32 throughout); anything
- *   else gives FA_ERR_UNSUPPORTED.  scale finite and > 0.
+ *   accumulation) and FA_F32 with 1 <= d <= 256 (fp32 throughout, the range
+ *   of the fp32 forward); anything else gives FA_ERR_UNSUPPORTED.  scale
+ *   finite and > 0.
  */
 fa_status fa_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO,
                       const float *LSE, void *dQ, void *dK, void *dV,

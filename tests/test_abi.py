@@ -231,7 +231,7 @@ def test_backward_workspace_and_arguments(lib):
     bad, uns = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
     assert bwd(dtype=5) == bad and bwd(B=-1) == bad and bwd(causal=2) == bad
     assert bwd(scale=float("inf")) == bad
-    assert bwd(dtype=fa.FA_F32, d=160) == uns and bwd(d=96) == uns and bwd(scale=-1.0) == uns
+    assert bwd(dtype=fa.FA_F32, d=257) == uns and bwd(d=96) == uns and bwd(scale=-1.0) == uns
     assert bwd(dO=None) == bad and bwd(LSE=None) == bad and bwd(dK=None) == bad
     assert bwd(dQ=P + 8) == bad and bwd(LSE=P + 2) == bad
     assert bwd(ws=None) == bad and bwd(ws_bytes=16) == bad

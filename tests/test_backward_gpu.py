@@ -213,9 +213,10 @@ def test_full_size_long_d128_shape():
                   nthreads=host_threads())
 
 
-@pytest.mark.parametrize("d", [1, 16, 40, 64, 100, 128])
+@pytest.mark.parametrize("d", [1, 16, 40, 64, 100, 128, 129, 200, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_f32_head_dims(d, causal):
+    # up to d = 128 four lanes share a row, beyond it sixteen (16-row workgroups)
     q, k, v, do, kl = make(1, 2, 150, 130, seed=d + 3, d=d, dtype=torch.float32)
     run_and_check(q, k, v, do, kl, causal, what=f"f32 d={d}")
 
