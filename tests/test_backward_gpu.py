@@ -221,9 +221,10 @@ def test_f32_head_dims(d, causal):
     run_and_check(q, k, v, do, kl, causal, what=f"f32 d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 200])
 @pytest.mark.parametrize("causal", [False, True])
-def test_f32_key_lens_ragged(causal):
-    q, k, v, do, kl = make(2, 3, 97, 211, seed=23, key_lens=[150, 0], d=64, dtype=torch.float32)
-    run_and_check(q, k, v, do, kl, causal, what="f32 key_lens")
-    q, k, v, do, kl = make(1, 2, 211, 97, seed=24, d=64, dtype=torch.float32)
-    run_and_check(q, k, v, do, kl, causal, scale=0.2, what="f32 N > Nk")
+def test_f32_key_lens_ragged(causal, d):
+    q, k, v, do, kl = make(2, 3, 97, 211, seed=23, key_lens=[150, 0], d=d, dtype=torch.float32)
+    run_and_check(q, k, v, do, kl, causal, what=f"f32 key_lens d={d}")
+    q, k, v, do, kl = make(1, 2, 211, 97, seed=24, d=d, dtype=torch.float32)
+    run_and_check(q, k, v, do, kl, causal, scale=0.2, what=f"f32 N > Nk d={d}")
