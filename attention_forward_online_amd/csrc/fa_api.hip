@@ -122,7 +122,8 @@ fa_status check_decode(const void *Q, const void *K, const void *V, void *O, flo
     if (B < 0 || H < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
     if (num_splits < 1) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_BF16 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_F32 && d > 256) return FA_ERR_UNSUPPORTED;
     if (num_splits > 256) return FA_ERR_UNSUPPORTED;
     if (scale <= 0.f) return FA_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA_OK;

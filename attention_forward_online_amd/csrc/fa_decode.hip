@@ -116,15 +116,22 @@ __device__ __forceinline__ void merge_state(float &ms, float &l, float *o, float
     ms = m;
 }
 
-template <typename T, int D>
+// GEN (fp32 only): rows of any width d <= D.  Lane cl of a row still holds
+// columns 4 cl .. 4 cl + 3; those at or past d read as 0, so they add nothing
+// to the dot products and their o stays 0.  Rows of a width that is not a
+// multiple of 4 are not 16-byte aligned and are read element by element.
+template <typename T, int D, bool GEN>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
-    float *__restrict__ ws, const int32_t *__restrict__ key_lens, int H, int Nk, int S, float c) {
+    float *__restrict__ ws, const int32_t *__restrict__ key_lens, int H, int Nk, int S, float c,
+    int d) {
     constexpr int EPL = Elem<T>::kPerLane;   // elements per lane (16 bytes)
     constexpr int LPR = D / EPL;             // lanes per key row
     constexpr int RPW = 64 / LPR;            // key rows per wave-wide load
     constexpr int ROWS_IT = RPW * kUnroll;   // rows per wave per iteration
     static_assert(64 % LPR == 0, "row must fit a wave");
+    static_assert(!GEN || sizeof(T) == 4, "rows of any width: fp32 only");
+    const int dd = GEN ? d : D;              // row length (elements)
 
     __shared__ float sh_o[kWaves][D];
     __shared__ float sh_ms[kWaves], sh_l[kWaves];
@@ -136,11 +143,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int kl = visible_len(key_lens, b, Nk);
     const int chunk = (kl + S - 1) / S;
     const int k_begin = min(split * chunk, kl), k_end = min(k_begin + chunk, kl);
-    const T *kp = K + bh * Nk * D + cl * EPL;
-    const T *vp = V + bh * Nk * D + cl * EPL;
+    const T *kp = K + bh * Nk * dd + cl * EPL;
+    const T *vp = V + bh * Nk * dd + cl * EPL;
+    // this lane's 16 bytes of the row at p
+    [[maybe_unused]] const int ncol = dd - cl * EPL;   // columns of the row this lane holds (GEN)
+    auto load = [&](const T *p) -> u32x4_t {
+        if constexpr (!GEN) {
+            return __builtin_nontemporal_load((const u32x4_t *)p);
+        } else {
+            if (ncol >= EPL && (dd & 3) == 0) return __builtin_nontemporal_load((const u32x4_t *)p);
+            u32x4_t r = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                if (e < ncol) r[e] = __builtin_nontemporal_load((const uint32_t *)p + e);
+            return r;
+        }
+    };
 
     float q[EPL];
-    Elem<T>::widen(*(const u32x4_t *)(Q + bh * D + cl * EPL), q);
+    if constexpr (GEN)
+        Elem<T>::widen(load(Q + bh * dd + cl * EPL), q);
+    else
+        Elem<T>::widen(*(const u32x4_t *)(Q + bh * D + cl * EPL), q);
 
     // the running denominator is l + lc: each iteration's sum of weights is
     // added with an error-free two-sum whose rounding error accumulates in lc
@@ -155,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         for (int u = 0; u < kUnroll; ++u) {
             const int row = base + u * RPW + rg;
             const bool in = row < k_end;
-            kr[u] = in ? __builtin_nontemporal_load((const u32x4_t *)(kp + (size_t)row * D)) : u32x4_t{0, 0, 0, 0};
-            vr[u] = in ? __builtin_nontemporal_load((const u32x4_t *)(vp + (size_t)row * D)) : u32x4_t{0, 0, 0, 0};
+            kr[u] = in ? load(kp + (size_t)row * dd) : u32x4_t{0, 0, 0, 0};
+            vr[u] = in ? load(vp + (size_t)row * dd) : u32x4_t{0, 0, 0, 0};
         }
         float s[kUnroll];
 #pragma unroll
@@ -218,26 +242,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     // merge the waves; one thread per output column
     const size_t rec = bh * S + split;
     const size_t nrec = (size_t)gridDim.z * H * S;
-    for (int col = tid; col < D; col += kThreads) {
+    for (int col = tid; col < dd; col += kThreads) {
         float m = sh_ms[0], lw = sh_l[0], ow = sh_o[0][col];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) merge_state<1>(m, lw, &ow, sh_ms[w], sh_l[w], &sh_o[w][col]);
-        ws[rec * D + col] = ow;
+        ws[rec * dd + col] = ow;
         if (col == 0) {
-            ws[nrec * D + rec] = m;
-            ws[nrec * D + nrec + rec] = lw;
+            ws[nrec * dd + rec] = m;
+            ws[nrec * dd + nrec + rec] = lw;
         }
     }
 }
 
-template <typename T, int D>
+// one thread per column; with GEN the threads of columns at or past d write
+// nothing
+template <typename T, int D, bool GEN>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
-    const float *__restrict__ ws, T *__restrict__ O, float *__restrict__ LSE, int BH, int S) {
+    const float *__restrict__ ws, T *__restrict__ O, float *__restrict__ LSE, int BH, int S, int d) {
     const int bh = blockIdx.x, col = threadIdx.x;
+    const int dd = GEN ? d : D;
     const size_t nrec = (size_t)BH * S;
-    const float *wo = ws + (size_t)bh * S * D;
-    const float *wm = ws + nrec * D + (size_t)bh * S;
-    const float *wl = ws + nrec * D + nrec + (size_t)bh * S;
+    const float *wo = ws + (size_t)bh * S * dd;
+    const float *wm = ws + nrec * dd + (size_t)bh * S;
+    const float *wl = ws + nrec * dd + nrec + (size_t)bh * S;
     float m = neg_inf();
     for (int s = 0; s < S; ++s) m = fmaxf(m, wm[s]);
     const float ref = m == neg_inf() ? 0.f : m;
@@ -245,29 +272,33 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
     for (int s = 0; s < S; ++s) {   // fixed order: deterministic
         const float w = exp2_hw(wm[s] - ref);
         l = fmaf(w, wl[s], l);
-        o = fmaf(w, wo[(size_t)s * D + col], o);
+        if (!GEN || col < dd) o = fmaf(w, wo[(size_t)s * dd + col], o);
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    // pairs of columns for bf16 stores
     const float mine = o * inv;
-    const float nbr = __shfl_xor(mine, 1, 64);
-    if ((col & 1) == 0) {
-        float pair[2] = {mine, nbr};
-        Elem<T>::store(O + (size_t)bh * D + col, pair, 2);
+    if constexpr (GEN) {
+        if (col < dd) O[(size_t)bh * dd + col] = mine;
+    } else {
+        // pairs of columns for bf16 stores
+        const float nbr = __shfl_xor(mine, 1, 64);
+        if ((col & 1) == 0) {
+            float pair[2] = {mine, nbr};
+            Elem<T>::store(O + (size_t)bh * D + col, pair, 2);
+        }
     }
     if (col == 0) LSE[bh] = l > 0.f ? (m + log2_hw(l)) * kLn2 : neg_inf();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool GEN = false>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits, a.H, a.B), dim3(kThreads), 0,
-                       stream, (const T *)a.Q, (const T *)a.K, (const T *)a.V, a.workspace,
-                       a.key_lens, a.H, a.Nk, a.num_splits, c);
+    hipLaunchKernelGGL((decode_split_kernel<T, D, GEN>), dim3(a.num_splits, a.H, a.B), dim3(kThreads),
+                       0, stream, (const T *)a.Q, (const T *)a.K, (const T *)a.V, a.workspace,
+                       a.key_lens, a.H, a.Nk, a.num_splits, c, a.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(D), 0, stream,
-                       (const float *)a.workspace, (T *)a.O, a.LSE, a.B * a.H, a.num_splits);
+    hipLaunchKernelGGL((decode_combine_kernel<T, D, GEN>), dim3(a.B * a.H), dim3(D), 0, stream,
+                       (const float *)a.workspace, (T *)a.O, a.LSE, a.B * a.H, a.num_splits, a.d);
     return hipGetLastError();
 }
 
@@ -275,7 +306,13 @@ hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream) {
     if (is_bf16) return a.d == 64 ? launch_t<uint16_t, 64>(a, stream) : launch_t<uint16_t, 128>(a, stream);
-    return a.d == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
+    if (a.d == 64) return launch_t<float, 64>(a, stream);
+    if (a.d == 128) return launch_t<float, 128>(a, stream);
+    // fp32 rows of other widths: the smallest lane layout that holds them
+    if (a.d <= 16) return launch_t<float, 16, true>(a, stream);
+    if (a.d <= 64) return launch_t<float, 64, true>(a, stream);
+    if (a.d <= 128) return launch_t<float, 128, true>(a, stream);
+    return launch_t<float, 256, true>(a, stream);
 }
 
 }  // namespace fa

@@ -101,7 +101,8 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *   num_splits) bytes, 16-byte aligned, owned by the caller; its contents on
  *   entry do not matter and are overwritten.  Two calls that share a
  *   workspace must not overlap in time (same stream, or synchronised).
- *   Supported: FA_BF16 and FA_F32 with d in {64, 128}; 1 <= num_splits <= 256.
+ *   Supported: FA_BF16 with d in {64, 128}, FA_F32 with 1 <= d <= 256 (the
+ *   range of the fp32 forward); 1 <= num_splits <= 256.
  */
 fa_status fa_decode_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
                             int B, int H, int Nk, int d, float scale,

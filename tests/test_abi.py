@@ -135,6 +135,8 @@ def test_decode_rejects_bad_arguments(lib):
     assert dec(lib, B=70000, ws_bytes=1 << 40) == bad
     assert dec(lib, B=1, H=1, Nk=1 << 23, ws_bytes=1 << 20) == bad
     assert dec(lib, d=96) == uns and dec(lib, d=256) == uns
+    # fp32 rows of any width up to 256, as the fp32 forward
+    assert dec(lib, d=257, dtype=fa.FA_F32) == uns
     assert dec(lib, S=257, ws_bytes=1 << 30) == uns
     assert dec(lib, scale=0.0) == uns
     assert dec(lib, Q=None, K=None, V=None, O=None, LSE=None, ws=None, B=0) == fa.FA_OK

@@ -248,6 +248,23 @@ def test_decode_key_lens_and_empty(dtype):
     _decode_check(inp, 4, "decode Nk=0")
 
 
+@pytest.mark.parametrize("d", [1, 3, 16, 17, 40, 100, 129, 200, 256])
+@pytest.mark.parametrize("S", [1, 16])
+def test_decode_f32_widths(d, S):
+    # fp32 rows of widths other than 64 and 128 (the lanes past d hold zeros;
+    # widths that are not a multiple of 4 are read element by element), with a
+    # key length, an empty batch and a short one; the result equals the fp32
+    # forward's with one query to rounding
+    inp = random_case(3, 2, 1, 700, d, F32, seed=d + S, device=DEV, key_lens=[700, 0, 333])
+    _, _, o, lse = _decode_check(inp, S, f"decode f32 d={d}")
+    o_f, l_f = fa.attention(inp["q"], inp["k"], inp["v"], key_lens=inp["key_lens"])
+    torch.cuda.synchronize()
+    assert torch.allclose(o, o_f, rtol=0, atol=2e-6)
+    assert torch.equal(torch.isinf(lse), torch.isinf(l_f))
+    fin = torch.isfinite(l_f)
+    assert torch.allclose(lse[fin], l_f[fin], rtol=0, atol=5e-6)
+
+
 def test_decode_matches_forward_and_split_invariance():
     inp = random_case(4, 4, 1, 3000, 128, F32, seed=8, device=DEV, key_lens=[3000, 2047, 1, 512])
     q, k, v, kl = inp["q"], inp["k"], inp["v"], inp["key_lens"]
