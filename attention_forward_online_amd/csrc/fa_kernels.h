@@ -56,7 +56,8 @@ int device_cu_count();
 
 // fp32 prefill, 1 <= d <= 256: fp32 FMA tiles.
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
-// split-KV decode, d in {64, 128}; is_bf16 selects the element type.
+// split-KV decode: bf16 with d in {64, 128}, fp32 with 1 <= d <= 256; is_bf16
+// selects the element type.
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t stream);
 // The decode's fixed per-GPU scratch (used in place of a caller workspace):
 // its size, and its device address on the current GPU.
@@ -73,7 +74,7 @@ hipError_t launch_fwd_v1(const FwdArgs &a, void *workspace, hipStream_t stream);
 // bf16 backward, d in {64, 128}: dQ, dK, dV from Q, K, V, O, dO and the forward's LSE.
 size_t backward_workspace_bytes(long long B, long long H, long long N);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
-// fp32 backward, 1 <= d <= 128 (same workspace layout).
+// fp32 backward, 1 <= d <= 256 (same workspace layout).
 hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t stream);
 // Test hook: polls of the one-pass wait before its fallback (< 0: default).
 void set_softmax_spin_limit(int limit);
