@@ -650,9 +650,9 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
 // P of tile t in registers while the dS side reads P(t - 1) and makes dP and
 // dS; after it the P side writes P(t) into the one P buffer and adds dV while
 // the dS side adds dK; the second barrier publishes P(t) and the loaded tile.
-// Each tile's S and P are made once and its Q/dO cross HBM once (two
-// launches, one per gradient, make S twice), and every P, dS and gradient
-// comes from the same operations in the same order as in those two launches.
+// Each tile's S and P are made once and its Q/dO cross HBM once (a launch
+// per gradient would make S twice and read Q and dO twice); each gradient
+// accumulator adds its tiles' terms in tile order.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
