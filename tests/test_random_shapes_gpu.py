@@ -1,10 +1,12 @@
 """Seeded random-shape sweep against the fp64 oracle: the bf16 prefill forward
-and backward, the fp32 forward at random head dims, and the split-KV decode.
+and backward, the fp32 forward and backward at random head dims, and the
+split-KV decode (bf16 and fp32 at d = 64, 128; fp32 at random widths).
 Query and key lengths from 1 to 700 (so workgroups hold partial query blocks,
 waves with no rows, and odd and even tile counts), causal or not, with or
 without per-batch key lengths (including 0 and values past Nk).  Same
 tolerances as the fixed-shape tests (bf16 forward 2e-2 on O, 1e-3 on LSE; fp32
-1e-5 on both; backward 8e-3 of the largest gradient entry + 1e-3), and rows or
+1e-5 on both; backward 8e-3 of the largest gradient entry + 1e-3, fp32
+backward 2e-5 of it + 1e-6), and rows or
 keys that see nothing must be exactly zero."""
 from __future__ import annotations
 
@@ -80,3 +82,32 @@ def test_decode_random_shape(seed):
     O_ref, L_ref = oracle.attention(to_host(q), to_host(k), to_host(v),
                                     scale=float(np.float32(1 / np.sqrt(d))), key_lens=kl)
     compare(o, lse, O_ref, L_ref, dtype, f"decode random seed {seed}")
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_f32_backward_random_shape(seed):
+    B, H, N, Nk, causal, kl = draw(5000 + seed)
+    d = int(np.random.default_rng(5000 + seed).integers(1, 257))
+    q, k, v, do, klt = make(B, H, N, Nk, seed=seed + 70, key_lens=kl, d=d, dtype=torch.float32)
+    say(f"    random fp32 backward seed {seed} d={d}")
+    run_and_check(q, k, v, do, klt, causal, what=f"random fp32 backward seed {seed} d={d}")
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_f32_decode_random_width(seed):
+    rng = np.random.default_rng(6000 + seed)
+    B, H = int(rng.integers(1, 9)), int(rng.integers(1, 5))
+    Nk = int(rng.integers(0, 5000))
+    d = int(rng.integers(1, 257))
+    S = int(rng.integers(1, 65))
+    kl = None
+    if rng.random() < 0.5:
+        kl = [int(x) for x in rng.integers(-2, Nk + 40, size=B)]
+    inp = random_case(B, H, 1, Nk, d, torch.float32, seed=seed, device=DEV, key_lens=kl)
+    q, k, v, klt = inp["q"], inp["k"], inp["v"], inp["key_lens"]
+    say(f"[gpu] fp32 decode random seed {seed}: B={B} H={H} Nk={Nk} d={d} splits={S} key_lens={kl}")
+    o, lse = fa.decode(q, k, v, num_splits=S, key_lens=klt)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(to_host(q), to_host(k), to_host(v),
+                                    scale=float(np.float32(1 / np.sqrt(d))), key_lens=kl)
+    compare(o, lse, O_ref, L_ref, torch.float32, f"fp32 decode random seed {seed} d={d}")
