@@ -24,7 +24,8 @@
 //                     reads, and each lane ends with 16-byte pieces of its key's
 //                     dK and dV rows.  At d = 128 (bwd_dkdv_paired_kernel) two
 //                     waves share each 32 keys: one makes S, P and dV and hands
-//                     P to the other, which makes dP, dS and dK.
+//                     P (bf16, its dV operand) to the other, which makes dP, dS
+//                     and dK.
 // Masking follows the forward exactly: causal key j <= i + (Nk - N), keys at
 // or past key_lens[b] invisible; invisible pairs get P = 0, hence dS = 0.
 // Both streaming kernels load their tiles from HBM straight into LDS (buffer
@@ -55,6 +56,13 @@ constexpr int kTile = 64;    // keys per K/V tile (dQ) and queries per Q/dO tile
 // reads 2-way instead of the 4-way of a 16-byte pad).  An XOR swizzle that is
 // conflict-free for both measured slower at d = 64 (more address registers).
 template <int N_> struct IntC { static constexpr int value = N_; };
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two floats to two fp16 (round to nearest even, v_cvt_pk_f16_f32), packed lo|hi.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
 
 template <int D> constexpr int kRowElems = D == 64 ? D + 8 : D + 24;
 template <int D>
@@ -642,14 +650,16 @@ __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT > 1 ? 1 : 2) void bwd_dkd
 // both accumulators beside its operands): 8 waves, waves w and w + 4 take the
 // same 32 keys 32w .. 32w + 31 of the workgroup's 128 and share a SIMD.  Wave
 // w (P side) keeps the K fragment: S = Q K^T, P = 2^(s c - LSE2) and
-// dV^T += dO^T P; it hands its fp32 P to wave w + 4 through LDS.  Wave w + 4
-// (dS side) keeps the V fragment and runs one Q/dO tile behind:
-// dP - D = dO V^T - D, dS = P (dP - D) and dK^T += Q^T dS.  Iteration t: the
-// P side works on tile t, the dS side on tile t - 1, tile t + 1 loads (three
-// Q/dO stages).  Before the iteration's first barrier the P side makes S and
-// P of tile t in registers while the dS side reads P(t - 1) and makes dP and
-// dS; after it the P side writes P(t) into the one P buffer and adds dV while
-// the dS side adds dK; the second barrier publishes P(t) and the loaded tile.
+// dV^T += dO^T P; it hands P to wave w + 4 through LDS as fp16 pairs (P lies
+// in [0, 1], where fp16 keeps 11 significant bits).  Wave w + 4 (dS side) keeps the V fragment and runs
+// one Q/dO tile behind: dP - D = dO V^T - D, dS = P (dP - D) and
+// dK^T += Q^T dS.  Iteration t: the P side works on tile t, the dS side on
+// tile t - 1, tile t + 1 loads (three Q/dO stages).  P goes through two LDS
+// buffers chosen by tile parity, so one barrier per iteration suffices: the
+// P side makes S and P of tile t, stores P into buffer t mod 2 and adds dV;
+// the dS side reads P(t - 1) from the other buffer, makes dP and dS and adds
+// dK; the barrier at the end publishes P(t) and the loaded tile and puts
+// every read of a buffer before its next write.
 // Each tile's S and P are made once and its Q/dO cross HBM once (a launch
 // per gradient would make S twice and read Q and dO twice); each gradient
 // accumulator adds its tiles' terms in tile order.
@@ -669,9 +679,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE], Qs1[TILE], Qs2[TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Gs0[TILE], Gs1[TILE], Gs2[TILE];   // dO
     __shared__ __attribute__((aligned(16))) float LD0[2 * kTile], LD1[2 * kTile], LD2[2 * kTile];
-    // P of one tile, [key group][32-query block][register pair][lane][2]: each
-    // pair of a group is one 512-byte row, written and read as 8 bytes per lane
-    __shared__ __attribute__((aligned(1024))) float Ps[kWaves * 2 * 8 * 64 * 2];
+    // bf16 P of two tiles (tile parity), [parity][key group][32-query block]
+    // [half][lane][4 pairs]: each half of a block is one 1 KiB row, written and
+    // read as 16 bytes per lane
+    __shared__ __attribute__((aligned(1024))) uint32_t Pb[2 * kWaves * 2 * 2 * 64 * 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -760,7 +771,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
     // pushed the kernel past 256 VGPRs).
     const int row_lane0 = lds_at<D>(qperm, 8 * g);
     const int tr_lane0 = lds_at<D>(8 * g + trow, tcol);
-    const int pw_lane0 = wave * (2 * 8 * 128) + 2 * lane;
+    const int pw_lane0 = wave * (2 * 2 * 256) + 4 * lane;
     int row_lane = row_lane0, tr_lane = tr_lane0, pw_lane = pw_lane0;
     auto row_operand = [&](const uint16_t *R, int qb, int kk) {
         return *(const u32x4_t *)&R[row_lane + lds_at<D>(32 * qb, 16 * kk)];
@@ -805,7 +816,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
         constexpr int ST = decltype(st_c)::value, ST_PREV = (ST + 2) % 3, ST_NEXT = (ST + 1) % 3;
         pw_lane = pw_lane0;
         asm volatile("" : "+v"(pw_lane));
-        float *const pw = Ps + pw_lane;   // this key group's P rows
+        uint32_t *const pw = Pb + (t & 1) * (kWaves * 2 * 2 * 256) + pw_lane;         // P(t)
+        const uint32_t *const pr = Pb + ((t + 1) & 1) * (kWaves * 2 * 2 * 256) + pw_lane;   // P(t - 1)
         const bool load_next = t + 1 < ntiles;
         rsrc_t qr, gr;
         tile_src(t + 1, qr, gr);
@@ -846,18 +858,23 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
                     lv[2 * h] = *(const f32x4_t *)&LDc[i8];
                     lv[2 * h + 1] = *(const f32x4_t *)&LDc[i8 + 4];
                 }
-                // P of queries 2e, 2e + 1: fp32 in place of S, bf16 pair for dV
+                // P of queries 2e, 2e + 1: a bf16 pair for dV, an fp16 pair
+                // (P <= 1: eight times finer than bf16) for the dS side
+                uint32_t ph[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int v = 2 * e;
                     const float p0 = exp2_hw(fmaf(x[qb][v], c, -lv[e >> 1][v & 3]));
                     const float p1 = exp2_hw(fmaf(x[qb][v + 1], c, -lv[e >> 1][(v & 3) + 1]));
-                    x[qb][v] = p0;
-                    x[qb][v + 1] = p1;
                     pk[qb][e] = pack_bf16x2(p0, p1);
                     pin(pk[qb][e]);
+                    ph[e] = pack_f16x2(p0, p1);
                 }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    *(u32x4_t *)&pw[(2 * qb + hh) * 256] = u32x4_t{ph[4 * hh], ph[4 * hh + 1], ph[4 * hh + 2], ph[4 * hh + 3]};
             }
+            grad_mfmas(gst(ST), pk, [](int) {});
         } else if (act1) {
             const float *LDc = ldst(ST_PREV);
             const uint16_t *Gc = gst(ST_PREV);
@@ -879,33 +896,25 @@ __global__ __launch_bounds__(2 * kThreads, 1) void bwd_dkdv_paired_kernel(
                           x[i & 1] = mfma32(a, fr[i >> 1], x[i & 1]);
                           issue(i);
                       });
-            // dS from P(t - 1), written by the P side before the last barrier
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x2_t pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = *(const f32x2_t *)&pw[(8 * qb + e) * 128];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int v = 2 * e;
-                    pk[qb][e] = pack_bf16x2(pv[e][0] * x[qb][v], pv[e][1] * x[qb][v + 1]);
-                    pin(pk[qb][e]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NL; ++j) issue(j);
-        }
-        // P(t - 1) has been read: the P side may overwrite the buffer
-        __syncthreads();
-        if (act0) {
+            // dS from P(t - 1) (fp16 pairs), written by the P side before the last barrier
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) *(f32x2_t *)&pw[(8 * qb + e) * 128] = f32x2_t{x[qb][2 * e], x[qb][2 * e + 1]};
-            grad_mfmas(gst(ST), pk, [](int) {});
-        } else if (act1) {
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x4_t r = *(const u32x4_t *)&pr[(2 * qb + hh) * 256];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = 4 * hh + j, v = 2 * e;
+                        const f16x2_t hv = __builtin_bit_cast(f16x2_t, (uint32_t)r[j]);
+                        const float p0 = (float)hv[0], p1 = (float)hv[1];
+                        pk[qb][e] = pack_bf16x2(p0 * x[qb][v], p1 * x[qb][v + 1]);
+                        pin(pk[qb][e]);
+                    }
+                }
             grad_mfmas(qst(ST_PREV), pk, [](int) {});
+        } else {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) issue(j);
         }
         wait_vmem_all();
         __syncthreads();
