@@ -85,7 +85,13 @@ def test_graph_replays_forward_and_decode():
     qf = torch.empty((1, 2, 77, 64), device=DEV, dtype=torch.float32)
     kf, vf, of = torch.empty_like(qf), torch.empty_like(qf), torch.empty_like(qf)
     lf = torch.empty((1, 2, 77), device=DEV, dtype=torch.float32)
-    for t in (q, k, v, qd, qf, kf, vf):
+    # an fp32 decode of a width other than 64 and 128 (rows read element by element)
+    qg = torch.empty((2, 3, 1, 101), device=DEV, dtype=torch.float32)
+    kg = torch.empty((2, 3, 900, 101), device=DEV, dtype=torch.float32)
+    vg, og = torch.empty_like(kg), torch.empty_like(qg)
+    lg = torch.empty((2, 3, 1), device=DEV, dtype=torch.float32)
+    wsg = torch.empty(fa.fa_decode_workspace_bytes(2, 3, 101, 5) // 4, device=DEV, dtype=torch.float32)
+    for t in (q, k, v, qd, qf, kf, vf, qg, kg, vg):
         t.copy_(fresh(t.shape, t.dtype, 0))
 
     def step():
@@ -93,11 +99,12 @@ def test_graph_replays_forward_and_decode():
         fa.fa_decode_splitkv(qd, k, v, od, ld, 8, ws)
         fa.fa_forward(q, k, v, o2, lse2, causal=False, key_lens=kl)
         fa.fa_forward(qf, kf, vf, of, lf, causal=False)
+        fa.fa_decode_splitkv(qg, kg, vg, og, lg, 5, wsg)
 
     graph = capture(step)
     for r in range(3):
         say(f"[gpu] graphs: forward + decode replay {r}")
-        for i, t in enumerate((q, k, v, qd, qf, kf, vf)):
+        for i, t in enumerate((q, k, v, qd, qf, kf, vf, qg, kg, vg)):
             t.copy_(fresh(t.shape, t.dtype, 10 * r + i + 1))
         graph.replay()
         torch.cuda.synchronize()
@@ -105,11 +112,13 @@ def test_graph_replays_forward_and_decode():
         ode, lde = fa.decode(qd, k, v, num_splits=8)
         oe2, le2 = fa.attention(q, k, v, causal=False, key_lens=kl)
         oef, lef = fa.attention(qf, kf, vf, causal=False)
+        oeg, leg = fa.decode(qg, kg, vg, num_splits=5)
         torch.cuda.synchronize()
         assert same(o, oe) and same(lse, le), f"replay {r}: forward differs from eager"
         assert same(od, ode) and same(ld, lde), f"replay {r}: decode differs from eager"
         assert same(o2, oe2) and same(lse2, le2), f"replay {r}: key-split forward differs from eager"
         assert same(of, oef) and same(lf, lef), f"replay {r}: fp32 forward differs from eager"
+        assert same(og, oeg) and same(lg, leg), f"replay {r}: fp32 d=101 decode differs from eager"
 
 
 @pytest.mark.parametrize("cols", [3000, 70001, 262144])
@@ -132,9 +141,12 @@ def test_graph_replays_softmax(cols):
         assert same(y, ye) and same(lse, le), f"replay {r}: softmax differs from eager"
 
 
-def test_graph_replays_backward():
-    B, H, N, d = 1, 4, 200, 64
-    q = torch.empty((B, H, N, d), device=DEV, dtype=torch.bfloat16)
+@pytest.mark.parametrize("d,dtype", [(64, torch.bfloat16), (128, torch.bfloat16), (200, torch.float32)])
+def test_graph_replays_backward(d, dtype):
+    # d = 128: the paired dK/dV kernel (P through two LDS buffers by tile
+    # parity); fp32 d = 200: sixteen lanes per row
+    B, H, N = 1, 4, 200
+    q = torch.empty((B, H, N, d), device=DEV, dtype=dtype)
     k, v, do = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((B, H, N), device=DEV, dtype=torch.float32)
@@ -148,7 +160,7 @@ def test_graph_replays_backward():
 
     graph = capture(step)
     for r in range(3):
-        say(f"[gpu] graphs: forward + backward replay {r}")
+        say(f"[gpu] graphs: forward + backward d={d} {dtype} replay {r}")
         for i, t in enumerate((q, k, v, do)):
             t.copy_(fresh(t.shape, t.dtype, 50 + 10 * r + i))
         graph.replay()
