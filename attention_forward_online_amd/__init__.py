@@ -5,7 +5,8 @@ include/fa.h); this package only marshals torch tensors into that ABI.
 """
 from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_SCRATCH_LIMIT,
                  FA_ERR_UNSUPPORTED, FA_F32, fa_decode_scratch_bytes, fa_decode_splitkv_noalloc,
-                 FA_OK, FaError, attention, attention_backward, attention_v1, decode, fa_backward,
+                 FA_OK, FaError, attention, attention_backward, attention_v1, bind_backward,
+                 bind_forward, decode, fa_backward,
                  fa_forward_v1, fa_forward_v1_workspace_bytes,
                  fa_backward_workspace_bytes, fa_decode_splitkv, fa_decode_workspace_bytes,
                  fa_forward, fa_softmax, fa_softmax_workspace_bytes, load_library, softmax,
@@ -15,7 +16,8 @@ from .fa import (EXPORTS, FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_SCRATC
 
 __all__ = ["EXPORTS", "FA_BF16", "FA_ERR_HIP", "FA_ERR_INVALID_ARG", "FA_ERR_SCRATCH_LIMIT",
            "FA_ERR_UNSUPPORTED", "FA_F32", "fa_decode_scratch_bytes", "fa_decode_splitkv_noalloc",
-           "FA_OK", "FaError", "attention", "attention_backward", "attention_v1", "decode",
+           "FA_OK", "FaError", "attention", "attention_backward", "attention_v1", "bind_backward",
+           "bind_forward", "decode",
            "fa_backward", "fa_forward_v1", "fa_forward_v1_workspace_bytes",
            "fa_backward_workspace_bytes", "fa_decode_splitkv",
            "fa_decode_workspace_bytes", "fa_forward", "fa_softmax", "fa_softmax_workspace_bytes",

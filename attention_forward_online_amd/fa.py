@@ -146,14 +146,8 @@ def _launch(idx: int, stream, call):
         return call(handle())
 
 
-def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-               lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
-               key_lens: Optional[torch.Tensor] = None, stream=None) -> None:
-    """O, LSE <- attention(q, k, v) through the C entry point fa_forward.
-
-    q, o: [B,H,N,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,N]; key_lens: int32 [B] or None.
-    """
-    lib = _lib or load_library()
+def _forward_args(q, k, v, o, lse, scale, causal, key_lens):
+    """Checked arguments of fa_forward (all but the stream) and the GPU index."""
     _check_dev("q", q)
     idx = q.get_device()
     for n, t in (("k", k), ("v", v), ("o", o)):
@@ -170,11 +164,47 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
             raise ValueError("key_lens must have shape [B]")
     if scale is None:
         scale = 1.0 / (d ** 0.5)
-    st = _launch(idx, stream, lambda h: lib.fa_forward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d, float(scale),
-        int(bool(causal)), _ptr(key_lens), _dtype_code(q), h))
+    return idx, (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, Nk, d, float(scale),
+                 int(bool(causal)), _ptr(key_lens), _dtype_code(q))
+
+
+def _raise_on(st: int, where: str, lib) -> None:
     if st != FA_OK:
-        raise FaError(st, "fa_forward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+        raise FaError(st, where, lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+
+
+def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+               lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+               key_lens: Optional[torch.Tensor] = None, stream=None) -> None:
+    """O, LSE <- attention(q, k, v) through the C entry point fa_forward.
+
+    q, o: [B,H,N,d]; k, v: [B,H,Nk,d]; lse: float32 [B,H,N]; key_lens: int32 [B] or None.
+    """
+    lib = _lib or load_library()
+    idx, args = _forward_args(q, k, v, o, lse, scale, causal, key_lens)
+    _raise_on(_launch(idx, stream, lambda h: lib.fa_forward(*args, h)), "fa_forward", lib)
+
+
+def _bound(lib, fn, idx, stream, args, where):
+    """A launcher of fn(*args, stream handle) with the stream resolved now."""
+    h = _launch(idx, stream, lambda handle: handle)
+
+    def run() -> None:
+        st = fn(*args, h)
+        if st != FA_OK:
+            _raise_on(st, where, lib)
+    return run
+
+
+def bind_forward(q, k, v, o, lse, scale=None, causal=False, key_lens=None, stream=None):
+    """Check the arguments of fa_forward once and return a callable that runs it
+    again on the same buffers and stream (torch's current stream of the tensors'
+    GPU when binding, unless `stream` is given) without re-checking them: for
+    timed loops and serving loops whose buffers stay fixed.  The tensors must
+    outlive the callable."""
+    lib = _lib or load_library()
+    idx, args = _forward_args(q, k, v, o, lse, scale, causal, key_lens)
+    return _bound(lib, lib.fa_forward, idx, stream, args, "fa_forward")
 
 
 def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
@@ -330,15 +360,8 @@ def fa_backward_workspace_bytes(B: int, H: int, N: int) -> int:
     return int(load_library().fa_backward_workspace_bytes(B, H, N))
 
 
-def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=False,
-                key_lens=None, stream=None) -> None:
-    """dQ, dK, dV of sum(dO * O) through the C entry point fa_backward.
-
-    q, o, do, dq: [B,H,N,d]; k, v, dk, dv: [B,H,Nk,d] (bf16); lse: float32
-    [B,H,N] from fa_forward; workspace: a GPU tensor of at least
-    fa_backward_workspace_bytes(B, H, N) bytes.
-    """
-    lib = _lib or load_library()
+def _backward_args(q, k, v, o, do, lse, dq, dk, dv, workspace, scale, causal, key_lens):
+    """Checked arguments of fa_backward (all but the stream) and the GPU index."""
     _check_dev("q", q)
     idx = q.get_device()
     for n, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -358,12 +381,31 @@ def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=F
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = _launch(idx, stream, lambda h: lib.fa_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-        B, H, N, Nk, d, float(scale), int(bool(causal)), _ptr(key_lens), _ptr(workspace),
-        ws_bytes, _dtype_code(q), h))
-    if st != FA_OK:
-        raise FaError(st, "fa_backward", lib.fa_last_hip_error().decode() if st == FA_ERR_HIP else "")
+    return idx, (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                 _ptr(dv), B, H, N, Nk, d, float(scale), int(bool(causal)), _ptr(key_lens),
+                 _ptr(workspace), ws_bytes, _dtype_code(q))
+
+
+def fa_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=False,
+                key_lens=None, stream=None) -> None:
+    """dQ, dK, dV of sum(dO * O) through the C entry point fa_backward.
+
+    q, o, do, dq: [B,H,N,d]; k, v, dk, dv: [B,H,Nk,d] (bf16); lse: float32
+    [B,H,N] from fa_forward; workspace: a GPU tensor of at least
+    fa_backward_workspace_bytes(B, H, N) bytes.
+    """
+    lib = _lib or load_library()
+    idx, args = _backward_args(q, k, v, o, do, lse, dq, dk, dv, workspace, scale, causal, key_lens)
+    _raise_on(_launch(idx, stream, lambda h: lib.fa_backward(*args, h)), "fa_backward", lib)
+
+
+def bind_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal=False,
+                  key_lens=None, stream=None):
+    """fa_backward's arguments checked once; the returned callable runs it again on
+    the same buffers and stream without re-checking (see bind_forward)."""
+    lib = _lib or load_library()
+    idx, args = _backward_args(q, k, v, o, do, lse, dq, dk, dv, workspace, scale, causal, key_lens)
+    return _bound(lib, lib.fa_backward, idx, stream, args, "fa_backward")
 
 
 def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, key_lens=None):

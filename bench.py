@@ -22,17 +22,23 @@ Kernel durations: the K timed launches run back to back between two HIP
 events recorded on the stream the library launches on (torch's current
 stream); one call is one kernel launch for the prefill workloads, so the
 region divided by K is that kernel's average launch duration (plus the short
-gaps between launches).  The cold-start diagnostic also records an event after
-every launch to show the clock transient launch by launch.
+gaps between launches).  The forward and backward calls go through launchers
+bound once (bind_forward / bind_backward: arguments checked when bound, not on
+every call), so that the host keeps ahead of kernels of a few tens of
+microseconds.  The cold-start diagnostic also records an event after every
+launch to show the clock transient launch by launch.
 
-Order of the run.  After any idle gap (50 ms is enough) the MI355X's clock
+Clock state.  After any idle gap (50 ms is enough) the MI355X's clock
 controller answers a step to full matrix-core load with a dip: launches 3 to
 ~30 of the headline kernel run up to 30% slower (495 -> 640 -> 487 us) before
-the clock settles.  The driver's W = 5 warm-ups end inside that dip, so the
-run first times the headline cold (reported as `cold_start`, the same W and K),
-then the split-KV decode (its own record; 2.5 ms of HBM-bound work per call),
-and then times the headline again with the same W and K: that second
-measurement is `value`, the sustained rate a continuously loaded GPU delivers.
+the clock settles, and the short workloads see the same dip after the host
+work between sections.  Every measurement therefore first runs its own call
+untimed back to back for about 60 ms (the count is in `launch_log`), then the
+W warm-ups, then the K timed calls: each figure is the rate under sustained
+load, the state the headline is timed in.  The headline is also timed once
+at the very start with no such phase (`cold_start`, the same W and K), then
+the split-KV decode runs (its own record; 2.5 ms of HBM-bound work per call),
+then the headline is timed again: that is `value`.
 
 Measured ceilings (`ceilings`): right after the decode, a bare streaming read
 of the decode's K tensor; right after the headline, a bare stream of bf16
@@ -118,17 +124,40 @@ def softmax_bytes(w):
     return 2 * w.rows * w.cols * el + w.rows * 4
 
 
-def time_launches(fn, steps, warmup, per_launch=False):
-    """`warmup` untimed calls, a device synchronisation, then `steps`
-    back-to-back calls between two HIP events recorded on torch's current
-    stream (the stream the library launches on); synchronised again.  Returns
-    ms per step over that region.  With per_launch, an event is also recorded
-    after every call and the per-call durations are returned too (each event
-    between launches adds a few microseconds, so this is for diagnostics)."""
+SETTLE_MS = 60.0       # untimed back-to-back load before each measurement (see time_launches)
+LAUNCH_LOG = []        # [label, untimed calls, timed calls] per measurement, in run order
+
+
+def time_launches(fn, steps, warmup, per_launch=False, settle_ms=SETTLE_MS, label=""):
+    """Run `fn` back to back untimed for about `settle_ms` (a call count from
+    three timed calls), then `warmup` untimed calls, a device synchronisation,
+    then `steps` back-to-back calls between two HIP events recorded on torch's
+    current stream (the stream the library launches on); synchronised again.
+    Returns ms per step over that region.  The settle phase puts every
+    measurement in the same sustained-load clock state the headline is timed
+    in: after host work between sections the clock controller answers a step
+    to full load with a dip lasting tens of milliseconds, longer than W
+    warm-ups of a short kernel (settle_ms=0 times the dip on purpose).  With
+    per_launch, an event is also recorded after every call and the per-call
+    durations are returned too (each event between launches adds a few
+    microseconds, so this is for diagnostics)."""
     import torch
+    untimed = warmup
+    if settle_ms > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - t0) / 3, 1e-6)
+        n = min(max(int(settle_ms * 1e-3 / per + 0.5), 10), 5000)
+        for _ in range(n):
+            fn()
+        untimed += 3 + n
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    LAUNCH_LOG.append([label, untimed, steps])
     n_ev = steps + 1 if per_launch else 2
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev[0].record()
@@ -326,8 +355,8 @@ def main():
         lse = torch.empty(w.B, w.H, w.N, device=dev, dtype=torch.float32)
     if want("headline"):
         # cold start: the same W and K right away (context only, see the module doc)
-        ms_cold, per_cold = time_launches(lambda: fa.fa_forward(q, k, v, o, lse, causal=True), K, W,
-                                          per_launch=True)
+        ms_cold, per_cold = time_launches(fa.bind_forward(q, k, v, o, lse, causal=True), K, W,
+                                          per_launch=True, settle_ms=0, label="headline cold")
         out["cold_start"] = {"ms_per_step": round(ms_cold, 5),
                              "tflops": round(prefill_flops(w) / (ms_cold * 1e-3) / 1e12, 2),
                              "launches": launch_stats(per_cold),
@@ -343,7 +372,8 @@ def main():
         nb = fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.d, wd.num_splits)
         ws = torch.empty(nb // 4, device=dev, dtype=torch.float32)
         ms_d = time_launches(
-            lambda: fa.fa_decode_splitkv(di["q"], di["k"], di["v"], od, ld, wd.num_splits, ws), K, W)
+            lambda: fa.fa_decode_splitkv(di["q"], di["k"], di["v"], od, ld, wd.num_splits, ws), K, W,
+            label="decode")
         nbytes = decode_bytes(wd)
         gbs = nbytes / (ms_d * 1e-3) / 1e9
         out["decode"] = {
@@ -357,7 +387,8 @@ def main():
         # measured ceiling of the decode: a bare streaming read of its K tensor
         # (the same 16-byte nontemporal loads, no arithmetic, include/fa_probe.h)
         sink_r = torch.empty(PROBE_READ_BLOCKS * fa.PROBE_THREADS, dtype=torch.int32, device=dev)
-        ms_r = time_launches(lambda: fa.probe_read(di["k"], PROBE_READ_BLOCKS, sink_r), K, W)
+        ms_r = time_launches(lambda: fa.probe_read(di["k"], PROBE_READ_BLOCKS, sink_r), K, W,
+                             label="probe read")
         rbytes = di["k"].numel() * di["k"].element_size()
         read_gbs = rbytes / (ms_r * 1e-3) / 1e9
         ceilings["hbm_read_stream"] = {
@@ -372,7 +403,7 @@ def main():
     if want("headline"):
         # one fa_forward call launches exactly one kernel, fwd_bf16_kernel<128, causal>
         # (timed after the decode section: the clock has settled, see the module doc)
-        ms_step = time_launches(lambda: fa.fa_forward(q, k, v, o, lse, causal=True), K, W)
+        ms_step = time_launches(fa.bind_forward(q, k, v, o, lse, causal=True), K, W, label="headline")
         flops = prefill_flops(w)
         value = flops / (ms_step * 1e-3) / 1e12
         out.update({
@@ -397,7 +428,8 @@ def main():
         # registers, no softmax, no memory traffic, include/fa_probe.h), timed
         # right after the headline with the same clock state, W and K
         sink_m = torch.empty(PROBE_MFMA_BLOCKS * fa.PROBE_THREADS, dtype=torch.float32, device=dev)
-        ms_m = time_launches(lambda: fa.probe_mfma(PROBE_MFMA_BLOCKS, PROBE_MFMA_ITERS, sink_m), K, W)
+        ms_m = time_launches(lambda: fa.probe_mfma(PROBE_MFMA_BLOCKS, PROBE_MFMA_ITERS, sink_m), K, W,
+                             label="probe mfma")
         mfl = PROBE_MFMA_BLOCKS * PROBE_MFMA_ITERS * fa.PROBE_MFMA_FLOPS
         mfma_tflops = mfl / (ms_m * 1e-3) / 1e12
         ceilings["mfma_bf16_stream"] = {
@@ -422,8 +454,8 @@ def main():
         oo = torch.empty_like(oi["q"])
         ol = torch.empty(wo.B, wo.H, wo.N, device=dev, dtype=torch.float32)
         kl = oi["key_lens"]
-        ms_o = time_launches(
-            lambda: fa.fa_forward(oi["q"], oi["k"], oi["v"], oo, ol, causal=wo.causal, key_lens=kl), K, W)
+        ms_o = time_launches(fa.bind_forward(oi["q"], oi["k"], oi["v"], oo, ol, causal=wo.causal,
+                                             key_lens=kl), K, W, label=name)
         kll = kl.tolist() if kl is not None else None
         fl = prefill_flops(wo, kll)
         peak = PEAK_F32_TFLOPS if wo.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -453,7 +485,7 @@ def main():
         ls = torch.empty(wsm.rows, device=dev, dtype=torch.float32)
         nb = fa.fa_softmax_workspace_bytes(wsm.rows, wsm.cols, xs.dtype)
         wss = torch.empty(max(nb, 16) // 4, device=dev, dtype=torch.float32)
-        ms_s = time_launches(lambda: fa.fa_softmax(xs, ys, ls, wss), K, W)
+        ms_s = time_launches(lambda: fa.fa_softmax(xs, ys, ls, wss), K, W, label="softmax")
         nbytes = softmax_bytes(wsm)
         gbs = nbytes / (ms_s * 1e-3) / 1e9
         out["softmax"] = {
@@ -467,7 +499,7 @@ def main():
         # measured ceiling of the softmax: a bare streaming copy of X into Y (the
         # same bytes read and written, 16-byte nontemporal loads and stores,
         # include/fa_probe.h)
-        ms_c = time_launches(lambda: fa.probe_copy(xs, ys, PROBE_COPY_BLOCKS), K, W)
+        ms_c = time_launches(lambda: fa.probe_copy(xs, ys, PROBE_COPY_BLOCKS), K, W, label="probe copy")
         cbytes = 2 * xs.numel() * xs.element_size()
         copy_gbs = cbytes / (ms_c * 1e-3) / 1e9
         ceilings["hbm_copy_stream"] = {
@@ -497,8 +529,8 @@ def main():
             nbw = fa.fa_backward_workspace_bytes(wb.B, wb.H, wb.N)
             wsb = torch.empty(max(nbw, 16) // 4, device=dev, dtype=torch.float32)
             ms_b = time_launches(
-                lambda: fa.fa_backward(bi["q"], bi["k"], bi["v"], bo, dob, bl, dq, dk, dv, wsb, causal=True),
-                K, W)
+                fa.bind_backward(bi["q"], bi["k"], bi["v"], bo, dob, bl, dq, dk, dv, wsb, causal=True),
+                K, W, label="backward " + name)
             bflops = 2.5 * prefill_flops(wb)
             el = 2
             alg = 8 * wb.B * wb.H * wb.N * wb.d * el + wb.B * wb.H * wb.N * 4
@@ -524,8 +556,9 @@ def main():
         nv1 = fa.fa_forward_v1_workspace_bytes(wv.B, wv.H, wv.N, wv.d)
         wv1 = torch.empty(max(nv1, 16) // 4, device=dev, dtype=torch.float32)
         ms_v1 = time_launches(lambda: fa.fa_forward_v1(vi["q"], vi["k"], vi["v"], o1, l1, wv1, causal=True),
-                                 K, W)
-        ms_v2 = time_launches(lambda: fa.fa_forward(vi["q"], vi["k"], vi["v"], o1, l1, causal=True), K, W)
+                              K, W, label="v1")
+        ms_v2 = time_launches(fa.bind_forward(vi["q"], vi["k"], vi["v"], o1, l1, causal=True), K, W,
+                              label="v1 ablation v2 leg")
         fl = prefill_flops(wv)
         out["v1_ablation"] = {
             "workload": wv.describe() + " in the V1 loop order (KV outer, Q inner, O/m/l via HBM)",
@@ -550,8 +583,9 @@ def main():
             try:
                 for rn, code in rules:
                     fa.testing_set_rescale_rule(code)
-                    ms_r = time_launches(lambda: fa.fa_forward(ri["q"], ri["k"], ri["v"], ro, rl,
-                                                                  causal=wr.causal, key_lens=kl), K, W)
+                    ms_r = time_launches(fa.bind_forward(ri["q"], ri["k"], ri["v"], ro, rl,
+                                                         causal=wr.causal, key_lens=kl), K, W,
+                                         label=f"rescale {rn} {name}")
                     rec[rn + "_ms"] = round(ms_r, 5)
             finally:
                 fa.testing_set_rescale_rule(fa.RESCALE_GUARD)
@@ -596,6 +630,7 @@ def main():
         del O_ref, L_ref, og, lg
     if ceilings:
         out["ceilings"] = ceilings
+    out["launch_log"] = LAUNCH_LOG
     print(json.dumps(out), flush=True)
 
 

@@ -52,6 +52,40 @@ def test_side_stream_matches_default_stream():
     assert all(same(a, b) for a, b in zip(g0, g1))
 
 
+def test_bound_launchers_match_the_checked_calls():
+    """bind_forward / bind_backward: bound once, run twice with new inputs copied
+    into the same buffers (and once on a side stream bound there), each result
+    bit-identical to the checked call on the same inputs."""
+    B, H, N, d = 2, 3, 257, 64
+    q = torch.empty((B, H, N, d), device=DEV, dtype=torch.bfloat16)
+    k, v, do = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), device=DEV, dtype=torch.float32)
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N) // 4, device=DEV, dtype=torch.float32)
+    kl = torch.tensor([190, 257], dtype=torch.int32, device=DEV)
+    fwd = fa.bind_forward(q, k, v, o, lse, causal=True, key_lens=kl)
+    bwd = fa.bind_backward(q, k, v, o, do, lse, dq, dk, dv, ws, causal=True, key_lens=kl)
+    for r in range(2):
+        say(f"[gpu] bound launchers: round {r}")
+        for i, t in enumerate((q, k, v, do)):
+            t.copy_(fresh(t.shape, t.dtype, 300 + 10 * r + i))
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        oe, le = fa.attention(q, k, v, causal=True, key_lens=kl)
+        ge = fa.attention_backward(q, k, v, oe, le, do, causal=True, key_lens=kl)
+        torch.cuda.synchronize()
+        assert same(o, oe) and same(lse, le), f"round {r}: bound forward differs"
+        assert all(same(a, b) for a, b in zip((dq, dk, dv), ge)), f"round {r}: bound backward differs"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o.zero_()
+    with torch.cuda.stream(side):
+        fa.bind_forward(q, k, v, o, lse, causal=True, key_lens=kl)()
+    side.synchronize()
+    assert same(o, oe) and same(lse, le), "bound forward on a side stream differs"
+
+
 def capture(fn):
     """Warm up on a side stream (torch's rule for capture), then capture fn."""
     side = torch.cuda.Stream()
