@@ -186,11 +186,16 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
 
 
 def _bound(lib, fn, idx, stream, args, where):
-    """A launcher of fn(*args, stream handle) with the stream resolved now."""
+    """A launcher of fn(*args, stream handle) with the stream resolved now; each
+    call runs with the tensors' GPU current, as the checked calls do."""
     h = _launch(idx, stream, lambda handle: handle)
 
     def run() -> None:
-        st = fn(*args, h)
+        if torch.cuda.current_device() == idx:
+            st = fn(*args, h)
+        else:
+            with torch.cuda.device(idx):
+                st = fn(*args, h)
         if st != FA_OK:
             _raise_on(st, where, lib)
     return run
