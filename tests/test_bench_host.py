@@ -1,6 +1,8 @@
 """Host logic of bench.py (no GPU): the algorithmic FLOP and byte counts it
 divides by, the kernel-source hash that decides whether the committed counter
-runs still describe the kernels, and the refusal of more than one GPU."""
+runs still describe the kernels, the settle / warm-up / timed sequence of a
+measurement (with torch's device calls replaced), and the refusal of more
+than one GPU."""
 from __future__ import annotations
 
 import os
@@ -130,3 +132,39 @@ def test_rescale_replay_counts():
     k = np.zeros((1, 128, 64)); k[0, 32:64, 0] = 40.0; k[0, 64:, 0] = 40.0
     r = bench.replay_rescales(q, k, float(np.log(2.0)), False, None, 64)
     assert r["guard"]["moves_per_row"] == 1.0     # the first tile's max (40) is taken up front
+
+
+def test_time_launches_settles_then_times(monkeypatch):
+    """The settle phase (a call count from three timed calls, clamped to
+    [10, 5000]) runs before the warm-ups, the timed region holds exactly the
+    K steps, and the launch log records the untimed and timed counts."""
+    import torch
+
+    calls = []
+    events = []
+
+    class FakeEvent:
+        def __init__(self, enable_timing=False):
+            self.t = None
+            events.append(self)
+
+        def record(self):
+            self.t = len(calls)
+
+        def elapsed_time(self, other):
+            return float(other.t - self.t)   # 1 ms per call in between
+
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    monkeypatch.setattr(torch.cuda, "Event", FakeEvent)
+    clock = iter([0.0, 0.003])
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: next(clock))
+    monkeypatch.setattr(bench, "LAUNCH_LOG", [])
+    ms = bench.time_launches(lambda: calls.append(1), 7, 2, settle_ms=60.0, label="x")
+    # 3 estimate calls took 3 ms -> 1 ms per call -> 60 settle calls
+    assert len(calls) == 3 + 60 + 2 + 7
+    assert ms == 1.0
+    assert bench.LAUNCH_LOG == [["x", 3 + 60 + 2, 7]]
+    # no settle phase: only the warm-ups before the timed region
+    del calls[:]
+    bench.time_launches(lambda: calls.append(1), 5, 4, settle_ms=0, label="cold")
+    assert len(calls) == 9 and bench.LAUNCH_LOG[-1] == ["cold", 4, 5]
