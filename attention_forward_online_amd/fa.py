@@ -185,9 +185,11 @@ def fa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
     _raise_on(_launch(idx, stream, lambda h: lib.fa_forward(*args, h)), "fa_forward", lib)
 
 
-def _bound(lib, fn, idx, stream, args, where):
+def _bound(lib, fn, idx, stream, args, where, tensors):
     """A launcher of fn(*args, stream handle) with the stream resolved now; each
-    call runs with the tensors' GPU current, as the checked calls do."""
+    call runs with the tensors' GPU current, as the checked calls do.  It holds
+    references to `tensors` (those whose addresses are in args), so they live
+    as long as the launcher does."""
     h = _launch(idx, stream, lambda handle: handle)
 
     def run() -> None:
@@ -198,6 +200,7 @@ def _bound(lib, fn, idx, stream, args, where):
                 st = fn(*args, h)
         if st != FA_OK:
             _raise_on(st, where, lib)
+    run.tensors = tuple(tensors)
     return run
 
 
@@ -205,11 +208,11 @@ def bind_forward(q, k, v, o, lse, scale=None, causal=False, key_lens=None, strea
     """Check the arguments of fa_forward once and return a callable that runs it
     again on the same buffers and stream (torch's current stream of the tensors'
     GPU when binding, unless `stream` is given) without re-checking them: for
-    timed loops and serving loops whose buffers stay fixed.  The tensors must
-    outlive the callable."""
+    timed loops and serving loops whose buffers stay fixed.  The callable keeps
+    the tensors alive; new inputs are copied into them in place."""
     lib = _lib or load_library()
     idx, args = _forward_args(q, k, v, o, lse, scale, causal, key_lens)
-    return _bound(lib, lib.fa_forward, idx, stream, args, "fa_forward")
+    return _bound(lib, lib.fa_forward, idx, stream, args, "fa_forward", (q, k, v, o, lse, key_lens))
 
 
 def fa_decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
@@ -410,7 +413,8 @@ def bind_backward(q, k, v, o, do, lse, dq, dk, dv, workspace, scale=None, causal
     the same buffers and stream without re-checking (see bind_forward)."""
     lib = _lib or load_library()
     idx, args = _backward_args(q, k, v, o, do, lse, dq, dk, dv, workspace, scale, causal, key_lens)
-    return _bound(lib, lib.fa_backward, idx, stream, args, "fa_backward")
+    return _bound(lib, lib.fa_backward, idx, stream, args, "fa_backward",
+                  (q, k, v, o, do, lse, dq, dk, dv, workspace, key_lens))
 
 
 def attention_backward(q, k, v, o, lse, do, scale=None, causal=False, key_lens=None):
